@@ -1,0 +1,12 @@
+"""PolyKV shared-pool hot path for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libpolykv.so`` (hand-written HIP kernels behind the C ABI in
+``include/polykv.h``); this package is its ctypes binding and build script.
+"""
+
+from .polykv import (  # noqa: F401
+    POLYKV_MAX_ROWS, POLYKV_PATH_AUTO, POLYKV_PATH_MFMA, POLYKV_PATH_VALU, PolyKVError,
+    lib, polykv_attend_shared, polykv_attend_shared_path, polykv_attend_workspace_bytes,
+    polykv_codebook_default, polykv_codebook_t, polykv_compress_k, polykv_compress_v,
+    polykv_layout_t, polykv_pool_layout, polykv_shape_t, polykv_strerror, pool_views,
+)

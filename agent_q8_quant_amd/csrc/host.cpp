@@ -1,0 +1,292 @@
+// Host side of the C ABI: layout arithmetic, the built-in codebook, argument validation
+// and kernel dispatch. Nothing here allocates device memory or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "polykv.h"
+#include "polykv_internal.h"
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+bool shape_ok(const polykv_shape_t& s) {
+    if (s.n_layers < 1 || s.n_kv_heads < 1 || s.n_tokens < 1) return false;
+    if (!(s.head_dim == 64 || s.head_dim == 128 || s.head_dim == 256))
+        return false;
+    // keep every per-tile and whole-pool quantity comfortably inside 63 bits
+    if (s.n_tokens > (1 << 26) || (int64_t)s.n_layers * s.n_kv_heads > (1 << 24)) return false;
+    return true;
+}
+
+int compute_layout(const polykv_shape_t& s, polykv_layout_t* out) {
+    if (!shape_ok(s)) return POLYKV_ERR_SHAPE;
+    const uint64_t T = (uint64_t)s.n_tokens, d = (uint64_t)s.head_dim;
+    const uint64_t tiles = (uint64_t)s.n_layers * (uint64_t)s.n_kv_heads;
+    const uint64_t groups = (T + 31) / 32;
+    polykv_layout_t l;
+    std::memset(&l, 0, sizeof(l));
+    l.shape = s;
+    l.k_codes_tile_stride = round_up(T * d, kAlign);
+    l.k_scales_tile_stride = round_up(T * (d / 32) * 2, kAlign);
+    l.v_planes_tile_stride = round_up(groups * 3 * d * 4, kAlign);
+    l.v_norms_tile_stride = round_up(T * 2, kAlign);
+    uint64_t off = 0;
+    l.k_codes_off = off;
+    off += tiles * l.k_codes_tile_stride;
+    l.k_scales_off = off;
+    off += tiles * l.k_scales_tile_stride;
+    l.v_planes_off = off;
+    off += tiles * l.v_planes_tile_stride;
+    l.v_norms_off = off;
+    off += tiles * l.v_norms_tile_stride;
+    l.total_bytes = off;
+    l.analytic_bytes = tiles * T * (d + 2 * (d / 32) + (3 * d) / 8 + 2);
+    *out = l;
+    return POLYKV_OK;
+}
+
+// ---- Lloyd-Max codebook for N(0,1), fp64 ----------------------------------------------
+
+double pdf(double x) {
+    if (std::isinf(x)) return 0.0;
+    return std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+}
+double upper_tail(double x) { return 0.5 * std::erfc(x / std::sqrt(2.0)); }
+double cell_mass(double a, double b) {
+    if (b <= 0.0) return cell_mass(-b, -a);
+    return upper_tail(a) - upper_tail(b);
+}
+
+polykv_codebook_t build_codebook() {
+    // Lloyd's iteration from evenly spaced centroids; the fixed point for the Gaussian is
+    // unique, so the start only changes the number of iterations.
+    double c[8];
+    for (int k = 0; k < 8; ++k) c[k] = -2.1 + 0.6 * k;
+    for (int it = 0; it < 100000; ++it) {
+        double t[9];
+        t[0] = -INFINITY;
+        t[8] = INFINITY;
+        for (int k = 0; k < 7; ++k) t[k + 1] = 0.5 * (c[k] + c[k + 1]);
+        double delta = 0.0;
+        for (int k = 0; k < 8; ++k) {
+            double mean = (pdf(t[k]) - pdf(t[k + 1])) / cell_mass(t[k], t[k + 1]);
+            delta = std::fmax(delta, std::fabs(mean - c[k]));
+            c[k] = mean;
+        }
+        if (delta < 1e-15) break;
+    }
+    polykv_codebook_t cb;
+    for (int k = 0; k < 8; ++k) cb.centroid[k] = (float)((c[k] - c[7 - k]) / 2.0);
+    for (int k = 0; k < 7; ++k)
+        cb.boundary[k] = (float)(((double)cb.centroid[k] + (double)cb.centroid[k + 1]) / 2.0);
+    return cb;
+}
+
+const polykv_codebook_t& default_codebook() {
+    static const polykv_codebook_t cb = build_codebook();
+    return cb;
+}
+
+bool codebook_ok(const polykv_codebook_t& cb) {
+    for (int k = 0; k < 8; ++k) {
+        if (!std::isfinite(cb.centroid[k]) || cb.centroid[k] != -cb.centroid[7 - k]) return false;
+        if (k < 7 && !(cb.centroid[k] < cb.centroid[k + 1])) return false;
+    }
+    for (int k = 0; k < 7; ++k) {
+        if (!std::isfinite(cb.boundary[k]) || cb.boundary[k] != -cb.boundary[6 - k]) return false;
+        if (k < 6 && !(cb.boundary[k] < cb.boundary[k + 1])) return false;
+    }
+    return cb.boundary[3] == 0.0f;
+}
+
+polykv::CodebookHalf half_of(const polykv_codebook_t& cb) {
+    polykv::CodebookHalf h;
+    for (int k = 0; k < 4; ++k) h.centroid_pos[k] = cb.centroid[4 + k];
+    for (int k = 0; k < 3; ++k) h.boundary_pos[k] = cb.boundary[4 + k];
+    return h;
+}
+
+// ---- validation ----------------------------------------------------------------------
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_layout(const polykv_layout_t* layout) {
+    if (!layout) return POLYKV_ERR_NULL;
+    polykv_layout_t want;
+    int rc = compute_layout(layout->shape, &want);
+    if (rc != POLYKV_OK) return rc;
+    if (std::memcmp(&want, layout, sizeof(want)) != 0) return POLYKV_ERR_LAYOUT;
+    return POLYKV_OK;
+}
+
+int check_layers(const polykv_layout_t& l, int32_t begin, int32_t count) {
+    if (count < 1 || begin < 0 || (int64_t)begin + count > l.shape.n_layers) return POLYKV_ERR_RANGE;
+    return POLYKV_OK;
+}
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return POLYKV_ERR_DEVICE;
+    }
+    // one entry per device ordinal; computed once, read many times
+    static std::mutex mu;
+    static int verdict[64];  // 0 unknown, 1 ok, -1 not gfx950
+    if (dev < 0 || dev >= 64) return POLYKV_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (verdict[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return POLYKV_ERR_DEVICE;
+        }
+        verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return verdict[dev] == 1 ? POLYKV_OK : POLYKV_ERR_DEVICE;
+}
+
+int launch_rc(hipError_t e) {
+    if (e != hipSuccess) return POLYKV_ERR_LAUNCH;
+    if (hipGetLastError() != hipSuccess) return POLYKV_ERR_LAUNCH;
+    return POLYKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int polykv_pool_layout(const polykv_shape_t* shape, polykv_layout_t* out) {
+    if (!shape || !out) return POLYKV_ERR_NULL;
+    return compute_layout(*shape, out);
+}
+
+int polykv_codebook_default(polykv_codebook_t* out) {
+    if (!out) return POLYKV_ERR_NULL;
+    *out = default_codebook();
+    return POLYKV_OK;
+}
+
+int polykv_compress_k(const void* k_fp16, void* pool, const polykv_layout_t* layout,
+                      int32_t layer_begin, int32_t layer_count, void* hip_stream) {
+    if (!k_fp16 || !pool || !layout) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (!aligned(pool, 256) || !aligned(k_fp16, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_compress_k(k_fp16, (uint8_t*)pool, polykv::make_geom(*layout),
+                                               layer_begin, layer_count, (hipStream_t)hip_stream));
+}
+
+int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* layout,
+                      const polykv_codebook_t* cb, int32_t layer_begin, int32_t layer_count,
+                      void* hip_stream) {
+    if (!v_fp16 || !pool || !layout) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (!aligned(pool, 256) || !aligned(v_fp16, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
+    const polykv_codebook_t& book = cb ? *cb : default_codebook();
+    if (!codebook_ok(book)) return POLYKV_ERR_CODEBOOK;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_compress_v(v_fp16, (uint8_t*)pool, polykv::make_geom(*layout),
+                                               half_of(book), layer_begin, layer_count,
+                                               (hipStream_t)hip_stream));
+}
+
+static int resolve_path(const polykv::PoolGeom& g, int32_t rows, int32_t path) {
+    if (path == POLYKV_PATH_AUTO)
+        return polykv::attend_mfma_supported(g, rows) && rows > 16 ? POLYKV_PATH_MFMA
+                                                                   : POLYKV_PATH_VALU;
+    return path;
+}
+
+size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_agents,
+                                     int32_t gqa, int32_t layer_count) {
+    if (!layout || check_layout(layout) != POLYKV_OK || n_agents < 1 || gqa < 1 || layer_count < 1)
+        return 0;
+    polykv::PoolGeom g = polykv::make_geom(*layout);
+    int rows = n_agents * gqa;
+    return polykv::attend_workspace_bytes(g, n_agents, gqa, layer_count,
+                                          resolve_path(g, rows, POLYKV_PATH_AUTO));
+}
+
+int polykv_attend_shared_path(const void* pool, const polykv_layout_t* layout,
+                              const polykv_codebook_t* cb, const float* q, float* out,
+                              int32_t n_agents, int32_t gqa, float softmax_scale,
+                              int32_t layer_begin, int32_t layer_count, void* workspace,
+                              size_t workspace_bytes, void* hip_stream, int32_t path) {
+    if (!pool || !layout || !q || !out) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (n_agents < 1 || gqa < 1) return POLYKV_ERR_SHAPE;
+    if (!aligned(pool, 256) || !aligned(q, 16) || !aligned(out, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
+    if ((int64_t)n_agents * gqa > POLYKV_MAX_ROWS) return POLYKV_ERR_RANGE;
+    if (!std::isfinite(softmax_scale)) return POLYKV_ERR_ARG;
+    if (path < POLYKV_PATH_AUTO || path > POLYKV_PATH_MFMA) return POLYKV_ERR_ARG;
+    const polykv_codebook_t& book = cb ? *cb : default_codebook();
+    if (!codebook_ok(book)) return POLYKV_ERR_CODEBOOK;
+    polykv::PoolGeom g = polykv::make_geom(*layout);
+    const int rows = n_agents * gqa;
+    path = resolve_path(g, rows, path);
+    if (path == POLYKV_PATH_MFMA && !polykv::attend_mfma_supported(g, rows)) return POLYKV_ERR_SHAPE;
+    size_t need = polykv::attend_workspace_bytes(g, n_agents, gqa, layer_count, path);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return POLYKV_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_device())) return rc;
+    polykv::AttendArgs a;
+    a.pool = (const uint8_t*)pool;
+    a.g = g;
+    a.cb = half_of(book);
+    a.q = q;
+    a.out = out;
+    a.n_agents = n_agents;
+    a.gqa = gqa;
+    a.layer_begin = layer_begin;
+    a.layer_count = layer_count;
+    a.softmax_scale = softmax_scale;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    hipStream_t s = (hipStream_t)hip_stream;
+    return launch_rc(path == POLYKV_PATH_MFMA ? polykv::launch_attend_mfma(a, s)
+                                              : polykv::launch_attend_valu(a, s));
+}
+
+int polykv_attend_shared(const void* pool, const polykv_layout_t* layout,
+                         const polykv_codebook_t* cb, const float* q, float* out,
+                         int32_t n_agents, int32_t gqa, float softmax_scale,
+                         int32_t layer_begin, int32_t layer_count, void* workspace,
+                         size_t workspace_bytes, void* hip_stream) {
+    return polykv_attend_shared_path(pool, layout, cb, q, out, n_agents, gqa, softmax_scale,
+                                     layer_begin, layer_count, workspace, workspace_bytes,
+                                     hip_stream, POLYKV_PATH_AUTO);
+}
+
+const char* polykv_strerror(int code) {
+    switch (code) {
+        case POLYKV_OK: return "ok";
+        case POLYKV_ERR_NULL: return "a required pointer is NULL";
+        case POLYKV_ERR_SHAPE: return "unsupported shape (head_dim, counts or sizes)";
+        case POLYKV_ERR_ALIGN: return "misaligned buffer (pool needs 256 B, others 16 B)";
+        case POLYKV_ERR_RANGE: return "layer range or rows per tile out of range";
+        case POLYKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case POLYKV_ERR_DEVICE: return "no HIP device or the device is not gfx950";
+        case POLYKV_ERR_LAUNCH: return "kernel launch failed";
+        case POLYKV_ERR_CODEBOOK: return "codebook not ascending, not symmetric, or boundary[3] != 0";
+        case POLYKV_ERR_LAYOUT: return "layout does not match polykv_pool_layout for its shape";
+        case POLYKV_ERR_ARG: return "argument out of its domain";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

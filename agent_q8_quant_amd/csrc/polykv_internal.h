@@ -1,0 +1,69 @@
+// Internal interface between the host layer (host.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "polykv.h"
+
+namespace polykv {
+
+// Everything a kernel needs to address one pool. Offsets are in bytes from the pool base.
+struct PoolGeom {
+    int32_t n_kv_heads, head_dim, n_tokens, n_groups;  // n_groups = ceil(T / 32)
+    uint64_t k_codes_off, k_codes_stride;
+    uint64_t k_scales_off, k_scales_stride;
+    uint64_t v_planes_off, v_planes_stride;
+    uint64_t v_norms_off, v_norms_stride;
+};
+
+inline PoolGeom make_geom(const polykv_layout_t& l) {
+    PoolGeom g;
+    g.n_kv_heads = l.shape.n_kv_heads;
+    g.head_dim = l.shape.head_dim;
+    g.n_tokens = l.shape.n_tokens;
+    g.n_groups = (l.shape.n_tokens + 31) / 32;
+    g.k_codes_off = l.k_codes_off;
+    g.k_codes_stride = l.k_codes_tile_stride;
+    g.k_scales_off = l.k_scales_off;
+    g.k_scales_stride = l.k_scales_tile_stride;
+    g.v_planes_off = l.v_planes_off;
+    g.v_planes_stride = l.v_planes_tile_stride;
+    g.v_norms_off = l.v_norms_off;
+    g.v_norms_stride = l.v_norms_tile_stride;
+    return g;
+}
+
+// Symmetric codebook as the kernels use it: the positive half only.
+struct CodebookHalf {
+    float centroid_pos[4];   // centroid[4..7]
+    float boundary_pos[3];   // boundary[4..6]; boundary[3] is 0
+};
+
+// Kernel launchers (defined in compress.hip / attend.hip). They return hipError_t of the
+// launch. Arguments are already validated.
+hipError_t launch_compress_k(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
+                             int32_t layer_begin, int32_t layer_count, hipStream_t s);
+hipError_t launch_compress_v(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
+                             const CodebookHalf& cb, int32_t layer_begin,
+                             int32_t layer_count, hipStream_t s);
+
+struct AttendArgs {
+    const uint8_t* pool;
+    PoolGeom g;
+    CodebookHalf cb;
+    const float* q;
+    float* out;
+    int32_t n_agents, gqa, layer_begin, layer_count;
+    float softmax_scale;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+size_t attend_workspace_bytes(const PoolGeom& g, int32_t n_agents, int32_t gqa,
+                              int32_t layer_count, int32_t path);
+hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s);
+bool attend_mfma_supported(const PoolGeom& g, int32_t rows);
+
+}  // namespace polykv

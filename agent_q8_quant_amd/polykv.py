@@ -1,0 +1,198 @@
+"""ctypes binding of ``libpolykv.so`` (C ABI in ``include/polykv.h``).
+
+Argument marshalling only: device buffers are torch tensors on the GPU, and every step
+of the hot path runs in the library's HIP kernels. If the library is not built, loading
+fails with an error; there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpolykv.so")
+
+POLYKV_OK = 0
+POLYKV_PATH_AUTO, POLYKV_PATH_VALU, POLYKV_PATH_MFMA = 0, 1, 2
+POLYKV_MAX_ROWS = 64
+
+EXPORTED_SYMBOLS = (
+    "polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k", "polykv_compress_v",
+    "polykv_attend_workspace_bytes", "polykv_attend_shared", "polykv_attend_shared_path",
+    "polykv_strerror",
+)
+
+
+class PolyKVError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__("%s failed: %s (%d)" % (where, polykv_strerror(code), code))
+        self.code = code
+
+
+class polykv_shape_t(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_tokens", ctypes.c_int32)]
+
+
+class polykv_layout_t(ctypes.Structure):
+    _fields_ = [("shape", polykv_shape_t),
+                ("k_codes_off", ctypes.c_uint64), ("k_codes_tile_stride", ctypes.c_uint64),
+                ("k_scales_off", ctypes.c_uint64), ("k_scales_tile_stride", ctypes.c_uint64),
+                ("v_planes_off", ctypes.c_uint64), ("v_planes_tile_stride", ctypes.c_uint64),
+                ("v_norms_off", ctypes.c_uint64), ("v_norms_tile_stride", ctypes.c_uint64),
+                ("analytic_bytes", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
+
+
+class polykv_codebook_t(ctypes.Structure):
+    _fields_ = [("centroid", ctypes.c_float * 8), ("boundary", ctypes.c_float * 7)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libpolykv.so is not built: run `python -m agent_q8_quant_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.polykv_pool_layout.argtypes = [ctypes.POINTER(polykv_shape_t), ctypes.POINTER(polykv_layout_t)]
+        L.polykv_codebook_default.argtypes = [ctypes.POINTER(polykv_codebook_t)]
+        L.polykv_compress_k.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t), i32, i32, vp]
+        L.polykv_compress_v.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t),
+                                        ctypes.POINTER(polykv_codebook_t), i32, i32, vp]
+        L.polykv_attend_workspace_bytes.argtypes = [ctypes.POINTER(polykv_layout_t), i32, i32, i32]
+        L.polykv_attend_workspace_bytes.restype = sz
+        att = [vp, ctypes.POINTER(polykv_layout_t), ctypes.POINTER(polykv_codebook_t), vp, vp,
+               i32, i32, ctypes.c_float, i32, i32, vp, sz, vp]
+        L.polykv_attend_shared.argtypes = att
+        L.polykv_attend_shared_path.argtypes = att + [i32]
+        L.polykv_strerror.argtypes = [ctypes.c_int]
+        L.polykv_strerror.restype = ctypes.c_char_p
+        for name in ("polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k",
+                     "polykv_compress_v", "polykv_attend_shared", "polykv_attend_shared_path"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def polykv_strerror(code: int) -> str:
+    return lib().polykv_strerror(int(code)).decode()
+
+
+def _check(rc, where):
+    if rc != POLYKV_OK:
+        raise PolyKVError(rc, where)
+
+
+def polykv_pool_layout(n_layers, n_kv_heads, head_dim, n_tokens) -> polykv_layout_t:
+    shape = polykv_shape_t(n_layers, n_kv_heads, head_dim, n_tokens)
+    out = polykv_layout_t()
+    _check(lib().polykv_pool_layout(ctypes.byref(shape), ctypes.byref(out)), "polykv_pool_layout")
+    return out
+
+
+def polykv_codebook_default() -> polykv_codebook_t:
+    cb = polykv_codebook_t()
+    _check(lib().polykv_codebook_default(ctypes.byref(cb)), "polykv_codebook_default")
+    return cb
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype != dtype or not t.is_contiguous():
+        raise TypeError("%s must be contiguous %s" % (name, dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _layers(layout, layer_begin, layer_count):
+    if layer_count is None:
+        layer_count = layout.shape.n_layers - layer_begin
+    return int(layer_begin), int(layer_count)
+
+
+def _kv_elems(layout, layer_count):
+    s = layout.shape
+    return layer_count * s.n_kv_heads * s.n_tokens * s.head_dim
+
+
+def polykv_compress_k(k, pool, layout, layer_begin=0, layer_count=None, stream=None):
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    if k.numel() != _kv_elems(layout, lc) or pool.numel() < layout.total_bytes:
+        raise ValueError("k or pool has the wrong size for the layout")
+    rc = lib().polykv_compress_k(_dev(k, torch.float16, "k"), _dev(pool, torch.uint8, "pool"),
+                                 ctypes.byref(layout), lb, lc, _stream_ptr(stream))
+    _check(rc, "polykv_compress_k")
+
+
+def polykv_compress_v(v, pool, layout, cb=None, layer_begin=0, layer_count=None, stream=None):
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    if v.numel() != _kv_elems(layout, lc) or pool.numel() < layout.total_bytes:
+        raise ValueError("v or pool has the wrong size for the layout")
+    rc = lib().polykv_compress_v(_dev(v, torch.float16, "v"), _dev(pool, torch.uint8, "pool"),
+                                 ctypes.byref(layout), ctypes.byref(cb) if cb is not None else None,
+                                 lb, lc, _stream_ptr(stream))
+    _check(rc, "polykv_compress_v")
+
+
+def polykv_attend_workspace_bytes(layout, n_agents, gqa, layer_count=None) -> int:
+    _, lc = _layers(layout, 0, layer_count)
+    return int(lib().polykv_attend_workspace_bytes(ctypes.byref(layout), n_agents, gqa, lc))
+
+
+def polykv_attend_shared_path(pool, layout, q, out, n_agents, gqa, softmax_scale, path,
+                              layer_begin=0, layer_count=None, cb=None, workspace=None,
+                              stream=None):
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    s = layout.shape
+    n = lc * n_agents * s.n_kv_heads * gqa * s.head_dim
+    if q.numel() != n or out.numel() != n or pool.numel() < layout.total_bytes:
+        raise ValueError("q, out or pool has the wrong size")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, torch.uint8, "workspace"), workspace.numel()
+    rc = lib().polykv_attend_shared_path(
+        _dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
+        ctypes.byref(cb) if cb is not None else None,
+        _dev(q, torch.float32, "q"), _dev(out, torch.float32, "out"),
+        int(n_agents), int(gqa), float(softmax_scale), lb, lc, ws_ptr, ws_bytes,
+        _stream_ptr(stream), int(path))
+    _check(rc, "polykv_attend_shared")
+
+
+def polykv_attend_shared(pool, layout, q, out, n_agents, gqa, softmax_scale, layer_begin=0,
+                         layer_count=None, cb=None, workspace=None, stream=None):
+    polykv_attend_shared_path(pool, layout, q, out, n_agents, gqa, softmax_scale,
+                              POLYKV_PATH_AUTO, layer_begin, layer_count, cb, workspace, stream)
+
+
+# ---- helpers for reading a pool back (views into a uint8 tensor; no arithmetic) --------
+
+def pool_views(pool, layout):
+    """Views of the four regions as [tiles][...] tensors (padding excluded)."""
+    s = layout.shape
+    tiles, T, d = s.n_layers * s.n_kv_heads, s.n_tokens, s.head_dim
+    G = (T + 31) // 32
+
+    def region(off, stride, nbytes):
+        r = pool[off:off + tiles * stride].view(tiles, stride)
+        return r[:, :nbytes]
+
+    kc = region(layout.k_codes_off, layout.k_codes_tile_stride, T * d).view(torch.int8).view(tiles, T, d)
+    ks = region(layout.k_scales_off, layout.k_scales_tile_stride, T * d // 16)
+    vp = region(layout.v_planes_off, layout.v_planes_tile_stride, G * 3 * d * 4)
+    vn = region(layout.v_norms_off, layout.v_norms_tile_stride, 2 * T)
+    return {"k_codes": kc,
+            "k_scales": ks.contiguous().view(torch.float16).view(tiles, T, d // 32),
+            "v_planes": vp.contiguous().view(torch.int32).view(tiles, G, 3, d),
+            "v_norms": vn.contiguous().view(torch.float16).view(tiles, T)}

@@ -1,0 +1,259 @@
+"""Benchmark of the PolyKV shared-pool hot path on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic workload: write-once
+compression of the fp16 K and V of every layer into the pool (compress_k + compress_v),
+then D decode steps of all agents against that pool (one attend_shared launch each).
+Inputs (fp16 K/V and the queries of all D decode steps) are resident in HBM before timing.
+
+Each kernel launch is timed with HIP events on the launch stream. Before every timed launch
+a 1 GiB buffer is read and written outside the events, which evicts the 256 MB Infinity
+Cache, so that the pool really comes from HBM (the default; --warm skips it).
+
+Prints ONE JSON line. value = whole-job agent-tokens/s = agents * D / (compress time +
+D * decode time), from the event times. Also reported: compress GB/s and decode GB/s over
+algorithmic bytes, each as a fraction of the 8 TB/s HBM peak, a roofline object for the
+decode kernel, and the CPU oracle timed on a bounded sample (cpu_baseline).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "shared-pool decode agent-tokens/s + compress GB/s, % of HBM peak"
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--config", default="3", help="workload index or name (default: the 4K Llama-3-8B pool)")
+    p.add_argument("--decode-steps", type=int, default=None, help="decode launches per step (default: the workload's)")
+    p.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
+    p.add_argument("--warm", action="store_true", help="do not evict the Infinity Cache between launches")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-layers", type=int, default=None)
+    p.add_argument("--mode", choices=["bench", "profile", "copy"], default="bench",
+                   help="profile: a few launches for rocprofv3 and no JSON; copy: a 1 GiB device copy "
+                        "for counter calibration")
+    return p.parse_args()
+
+
+def _src_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "agent_q8_quant_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_names, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key, {}).get(workload)
+    except (ValueError, AttributeError):
+        return None
+    if not rec or rec.get("source_sha") != _src_sha(src_names):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, n_layers_sample):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    from workloads import gen_k_layer, gen_q_step, gen_v_layer
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    c32, b32 = oracle.codebook_fp32()
+    tc = td = ta = 0.0
+    q = gen_q_step(cfg, 0)
+    for l in range(n_layers_sample):
+        k, v = gen_k_layer(cfg, l), gen_v_layer(cfg, l)
+        t = time.perf_counter()
+        pool = oracle.compress_pool(k, v, b32)
+        tc += time.perf_counter() - t
+        t = time.perf_counter()
+        kh, vh = oracle.dequant_pool(pool, c32)
+        td += time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.shared_pool_decode(q[l:l + 1], kh[None], vh[None], cfg.gqa, cfg.softmax_scale)
+        ta += time.perf_counter() - t
+    n = n_layers_sample
+    L, D = cfg.n_layers, cfg.decode_steps
+    job = (tc + td) / n * L + ta / n * L * D
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": cfg.n_agents * D / job, "unit": "agent-tokens/s",
+            "cores": int(blas_threads), "kind": "oracle",
+            "sample": "%d of %d layers: oracle compress + per-token dequant once, one decode step; "
+                      "job time = L/n * (compress + dequant) + L/n * D * decode" % (n, L),
+            "seconds_measured": round(tc + td + ta, 2),
+            "compress_GBps": (cfg.kv_elems * 4 + _analytic(cfg)) / ((tc / n) * L) / 1e9,
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
+            "host": platform.node()}
+
+
+def _analytic(cfg):
+    d = cfg.head_dim
+    return cfg.n_layers * cfg.n_kv_heads * cfg.n_tokens * (d + 2 * (d // 32) + 3 * d // 8 + 2)
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the pool would shard by KV head with no collective; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import agent_q8_quant_amd as pk
+    from workloads import config_by_name, gen_k_layer, gen_q_step, gen_v_layer
+
+    if not os.path.exists(os.path.join(ROOT, "agent_q8_quant_amd", "libpolykv.so")):
+        from agent_q8_quant_amd.build import build
+        build()
+    dev = torch.device("cuda", 0)
+
+    if args.mode == "copy":
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy of 1 GiB done x3", flush=True)
+        return
+
+    cfg = config_by_name(args.config)
+    D = args.decode_steps if args.decode_steps is not None else cfg.decode_steps
+    path = {"auto": pk.POLYKV_PATH_AUTO, "valu": pk.POLYKV_PATH_VALU, "mfma": pk.POLYKV_PATH_MFMA}[args.path]
+    lay = pk.polykv_pool_layout(cfg.n_layers, cfg.n_kv_heads, cfg.head_dim, cfg.n_tokens)
+
+    print("bench: generating %s" % cfg.name, file=sys.stderr, flush=True)
+    k = torch.empty((cfg.n_layers, cfg.n_kv_heads, cfg.n_tokens, cfg.head_dim), dtype=torch.float16, device=dev)
+    v = torch.empty_like(k)
+    for l in range(cfg.n_layers):
+        k[l].copy_(torch.from_numpy(gen_k_layer(cfg, l)))
+        v[l].copy_(torch.from_numpy(gen_v_layer(cfg, l)))
+    qshape = (cfg.n_layers, cfg.n_agents, cfg.n_q_heads, cfg.head_dim)
+    q = torch.empty((D,) + qshape, dtype=torch.float32, device=dev)
+    for s in range(D):
+        q[s].copy_(torch.from_numpy(gen_q_step(cfg, s)))
+    out = torch.empty(qshape, dtype=torch.float32, device=dev)
+    pool = torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev)
+    ws_bytes = pk.polykv_attend_workspace_bytes(lay, cfg.n_agents, cfg.gqa)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if not args.warm else None
+    torch.cuda.synchronize()
+
+    def evict():
+        if flush is not None:
+            flush.add_(1)
+
+    def timed(fn, ev_list):
+        evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ev_list.append((e0, e1))
+
+    def one_step(rec):
+        timed(lambda: pk.polykv_compress_k(k, pool, lay), rec["ck"])
+        timed(lambda: pk.polykv_compress_v(v, pool, lay), rec["cv"])
+        for s in range(D):
+            timed(lambda: pk.polykv_attend_shared_path(pool, lay, q[s], out, cfg.n_agents, cfg.gqa,
+                                                       cfg.softmax_scale, path, workspace=ws), rec["at"])
+
+    if args.mode == "profile":
+        rec = {"ck": [], "cv": [], "at": []}
+        for _ in range(max(1, args.steps)):
+            one_step(rec)
+        torch.cuda.synchronize()
+        print("profile run done: %d steps x (2 compress + %d decode) launches" % (args.steps, D), flush=True)
+        return
+
+    for _ in range(args.warmup):
+        one_step({"ck": [], "cv": [], "at": []})
+    torch.cuda.synchronize()
+    print("bench: warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    rec = {"ck": [], "cv": [], "at": []}
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    ms = {key: [a.elapsed_time(b) for a, b in rec[key]] for key in rec}
+    t_ck = sum(ms["ck"]) / len(ms["ck"]) / 1e3
+    t_cv = sum(ms["cv"]) / len(ms["cv"]) / 1e3
+    t_at = sum(ms["at"]) / len(ms["at"]) / 1e3
+    step_s = t_ck + t_cv + D * t_at
+
+    analytic = lay.analytic_bytes
+    fp16_bytes = cfg.kv_elems * 2
+    q_bytes = cfg.n_layers * cfg.n_agents * cfg.n_q_heads * cfg.head_dim * 4
+    compress_bytes = 2 * fp16_bytes + analytic
+    decode_bytes = analytic + 2 * q_bytes
+    compress_gbps = compress_bytes / (t_ck + t_cv) / 1e9
+    decode_gbps = decode_bytes / t_at / 1e9
+    workload = cfg.name
+    traffic = _traffic("attend", ["attend.hip"], workload)
+    result = {
+        "metric": METRIC,
+        "value": cfg.n_agents * D / step_s,
+        "unit": "agent-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+u3 pool; fp32 accumulate" + (" (fp16 MFMA operands)" if path == pk.POLYKV_PATH_MFMA else ""),
+        "data": "synthetic",
+        "config": {"workload": workload, "layers": cfg.n_layers, "kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "tokens": cfg.n_tokens, "agents": cfg.n_agents,
+                   "gqa": cfg.gqa, "decode_steps": D, "v_dist": cfg.v_dist,
+                   "cache": "warm" if args.warm else "infinity-cache evicted before each launch",
+                   "path": args.path},
+        "roofline": {"kernel": "attend_shared", "bound": "hbm", "achieved": decode_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": decode_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": decode_bytes,
+                     "avg_launch_us": t_at * 1e6},
+        "decode_agent_tokens_per_s": cfg.n_agents / t_at,
+        "decode_GBps": decode_gbps, "decode_frac_hbm": decode_gbps / HBM_PEAK_GBPS,
+        "compress_GBps": compress_gbps, "compress_frac_hbm": compress_gbps / HBM_PEAK_GBPS,
+        "compress_us": {"k": t_ck * 1e6, "v": t_cv * 1e6},
+        "compress_GBps_k": (fp16_bytes + cfg.kv_elems + cfg.kv_elems // 16) / t_ck / 1e9,
+        "compress_GBps_v": (fp16_bytes + cfg.kv_elems * 3 // 8
+                            + cfg.n_layers * cfg.n_kv_heads * cfg.n_tokens * 2) / t_cv / 1e9,
+        "wall_ms_per_step": wall / args.steps * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        n = args.cpu_sample_layers or max(1, min(cfg.n_layers, 4))
+        result["cpu_baseline"] = cpu_baseline(cfg, n)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * polykv.h - C ABI of the PolyKV shared-pool hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Method source: "PolyKV: A Shared Asymmetrically-Compressed KV Cache Pool for
+ * Multi-Agent LLM Inference", section "Abstract (arXiv)". Several agents share one KV
+ * pool that is compressed once: keys are quantised at int8 (q8_0), values with
+ * TurboQuant MSE (a Fast Walsh-Hadamard rotation followed by 3-bit Lloyd-Max codes with
+ * centroids for N(0,1)); every agent then decodes against that single pool.
+ *
+ * Definitions of the steps the abstract leaves open (these are the library's format):
+ *  - q8_0: blocks of 32 consecutive key entries along head_dim; fp16 scale
+ *    s = RNE16(amax / 127) with an IEEE float32 division; code q = RNE(x / s) with the
+ *    stored fp16 scale, clamped to [-127, 127]; s = 0 gives all codes 0.
+ *  - TurboQuant MSE: n = ||v||_2; y = H v / n (H the +-1 Sylvester Hadamard matrix, i.e.
+ *    the orthonormal FWHT of v * sqrt(d) / n); code = #{k : y > b_k} over the 7 codebook
+ *    boundaries (ties go to the lower code; n = 0 gives y = 0); fp16 RNE norm stored.
+ *  - Decode: out = softmax(scale * q . k_hat) . v_hat over every pool token, with
+ *    k_hat = q8 code * s and v_hat = (n16 / d) * H c[code]; query head j reads KV head
+ *    j / gqa.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_fp16, pool, q, out, workspace are DEVICE pointers; layout and
+ *    codebook structs are HOST pointers. The caller allocates and owns every buffer; the
+ *    library never allocates, frees or synchronises, and keeps no per-call state.
+ *  - hip_stream is a hipStream_t (NULL = the null stream). All device work is
+ *    asynchronous on it; buffers must stay alive until that work has completed.
+ *  - All arguments are validated on the host before anything is launched, so an error
+ *    return means nothing was enqueued. Non-finite inputs are not checked: the results
+ *    for them are unspecified.
+ *  - Return value: POLYKV_OK (0) or a negative POLYKV_ERR_* code.
+ */
+#ifndef POLYKV_H
+#define POLYKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define POLYKV_OK 0
+#define POLYKV_ERR_NULL (-1)       /* a required pointer is NULL                          */
+#define POLYKV_ERR_SHAPE (-2)      /* head_dim not in {64,128,256}, a count < 1, or       */
+                                   /* a size that overflows                               */
+#define POLYKV_ERR_ALIGN (-3)      /* pool not 256-B aligned, another buffer not 16-B     */
+#define POLYKV_ERR_RANGE (-4)      /* layer range outside the pool, or rows per tile      */
+                                   /* (n_agents * gqa) above POLYKV_MAX_ROWS              */
+#define POLYKV_ERR_WORKSPACE (-5)  /* workspace smaller than polykv_attend_workspace_bytes */
+#define POLYKV_ERR_DEVICE (-6)     /* no HIP device, or the current device is not gfx950  */
+#define POLYKV_ERR_LAUNCH (-7)     /* a kernel launch failed (hipGetLastError)             */
+#define POLYKV_ERR_CODEBOOK (-8)   /* codebook not ascending, not symmetric, or b[3] != 0 */
+#define POLYKV_ERR_LAYOUT (-9)     /* layout struct does not match polykv_pool_layout     */
+#define POLYKV_ERR_ARG (-10)       /* another argument out of its domain                  */
+
+#define POLYKV_MAX_ROWS 64         /* agents x query heads per KV head, per pool tile     */
+
+/* Pool geometry. */
+typedef struct {
+    int32_t n_layers;
+    int32_t n_kv_heads;
+    int32_t head_dim;   /* 64, 128 or 256 */
+    int32_t n_tokens;   /* >= 1 */
+} polykv_shape_t;
+
+/*
+ * Byte layout of a pool. The pool is one device buffer with four regions. A "tile" is
+ * one (layer, KV head) pair; tile index = layer * n_kv_heads + head. Inside a region,
+ * tile k starts at region_off + k * region_tile_stride; every tile stride is its payload
+ * rounded up to 256 B, and every region starts 256-B aligned.
+ *  k_codes : int8   [T][d]            per tile, row-major
+ *  k_scales: fp16   [T][d/32]         per tile
+ *  v_planes: uint32 [ceil(T/32)][3][d] per tile; bit j of word (g, p, i) is bit p of
+ *                                      the value code of token 32*g + j at coordinate i
+ *                                      (bits of tokens >= T are 0)
+ *  v_norms : fp16   [T]               per tile
+ * analytic_bytes counts the payload exactly (1 B per key code, 2 B per scale, 3 bits per
+ * value code, 2 B per norm); total_bytes is what the buffer must hold.
+ */
+typedef struct {
+    polykv_shape_t shape;
+    uint64_t k_codes_off, k_codes_tile_stride;
+    uint64_t k_scales_off, k_scales_tile_stride;
+    uint64_t v_planes_off, v_planes_tile_stride;
+    uint64_t v_norms_off, v_norms_tile_stride;
+    uint64_t analytic_bytes;
+    uint64_t total_bytes;
+} polykv_layout_t;
+
+/* 3-bit codebook: centroids ascending (code 0 is the most negative) and the 7 decision
+ * boundaries between them. The kernels require it symmetric about 0 with boundary[3] = 0. */
+typedef struct {
+    float centroid[8];
+    float boundary[7];
+} polykv_codebook_t;
+
+/*
+ * Fill *out with the pool layout for *shape. Host only; touches no device.
+ * Errors: NULL, SHAPE.
+ */
+int polykv_pool_layout(const polykv_shape_t* shape, polykv_layout_t* out);
+
+/*
+ * Fill *out with the library's Lloyd-Max codebook for N(0,1): Lloyd's iteration run in
+ * fp64 to a fixed point (centroids = conditional means of their cells, boundaries =
+ * midpoints), made exactly symmetric, centroids rounded to float32, boundaries = fp64
+ * midpoints of the float32 centroids rounded to float32. Computed once per process,
+ * thread-safe. Host only. Errors: NULL.
+ */
+int polykv_codebook_default(polykv_codebook_t* out);
+
+/*
+ * q8_0-compress keys into the pool (the "Keys are quantized at int8 (q8_0)" step).
+ *  k_fp16: device, IEEE binary16, contiguous [layer_count][n_kv_heads][n_tokens][head_dim]
+ *          holding pool layers [layer_begin, layer_begin + layer_count); 16-B aligned.
+ *  pool:   device, layout->total_bytes, 256-B aligned; only the k_codes and k_scales
+ *          tiles of those layers are written.
+ * Errors: NULL, ALIGN, RANGE, LAYOUT, DEVICE, LAUNCH.
+ */
+int polykv_compress_k(const void* k_fp16, void* pool, const polykv_layout_t* layout,
+                      int32_t layer_begin, int32_t layer_count, void* hip_stream);
+
+/*
+ * TurboQuant-MSE-compress values into the pool (the FWHT rotation + 3-bit Lloyd-Max
+ * step). v_fp16 as k_fp16 above; only the v_planes and v_norms tiles of those layers are
+ * written. cb: host pointer or NULL for polykv_codebook_default; only the boundaries are
+ * used. compress_k and compress_v write disjoint regions and may run concurrently.
+ * Errors: NULL, ALIGN, RANGE, LAYOUT, CODEBOOK, DEVICE, LAUNCH.
+ */
+int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* layout,
+                      const polykv_codebook_t* cb, int32_t layer_begin, int32_t layer_count,
+                      void* hip_stream);
+
+/* Decode kernel choice for polykv_attend_shared_path. */
+#define POLYKV_PATH_AUTO 0   /* the library's choice for the row count                    */
+#define POLYKV_PATH_VALU 1   /* fp32 vector-ALU contraction                               */
+#define POLYKV_PATH_MFMA 2   /* matrix-core contraction (fp16 operands, fp32 accumulate)  */
+
+/* Device bytes of workspace polykv_attend_shared needs for these arguments (0 if none). */
+size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_agents,
+                                     int32_t gqa, int32_t layer_count);
+
+/*
+ * One decode step of every agent against the shared pool (the "N independent agent
+ * contexts" reading one compressed pool). The pool is only read, so any number of calls
+ * may run concurrently on one pool.
+ *  q:   device fp32 [layer_count][n_agents][n_kv_heads * gqa][head_dim], 16-B aligned;
+ *       query head j of an agent attends KV head j / gqa.
+ *  out: device fp32, same shape as q; every element is written.
+ *  softmax_scale: multiplies q . k_hat before the softmax (normally 1/sqrt(head_dim)).
+ *  cb: host codebook or NULL for the default; only the centroids are used.
+ *  workspace: device, at least polykv_attend_workspace_bytes(...) bytes (may be NULL
+ *       when that is 0).
+ * Errors: NULL, SHAPE, ALIGN, RANGE, LAYOUT, CODEBOOK, WORKSPACE, DEVICE, LAUNCH.
+ */
+int polykv_attend_shared(const void* pool, const polykv_layout_t* layout,
+                         const polykv_codebook_t* cb, const float* q, float* out,
+                         int32_t n_agents, int32_t gqa, float softmax_scale,
+                         int32_t layer_begin, int32_t layer_count,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* As polykv_attend_shared with an explicit decode kernel (POLYKV_PATH_*). */
+int polykv_attend_shared_path(const void* pool, const polykv_layout_t* layout,
+                              const polykv_codebook_t* cb, const float* q, float* out,
+                              int32_t n_agents, int32_t gqa, float softmax_scale,
+                              int32_t layer_begin, int32_t layer_count,
+                              void* workspace, size_t workspace_bytes, void* hip_stream,
+                              int32_t path);
+
+/* Static English text for a return code. Never NULL. */
+const char* polykv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POLYKV_H */

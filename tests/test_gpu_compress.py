@@ -1,0 +1,150 @@
+"""GPU parity of the compress kernels against the oracle (keys bit-exact, values by rule)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import agent_q8_quant_amd as pk
+import oracle
+from workloads import CONFIGS, gen_k_layer, gen_v_layer
+
+from gpu_helpers import (B32, check_norms, check_v_codes, device, layout_for, new_pool,
+                         read_pool, upload_kv)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_compress_full_config(cfg):
+    _say("compress parity", cfg.name)
+    lay = layout_for(cfg)
+    k, v = upload_kv(cfg)
+    pool = new_pool(lay)
+    pk.polykv_compress_k(k, pool, lay)
+    pk.polykv_compress_v(v, pool, lay)
+    torch.cuda.synchronize()
+    del k, v
+    got = read_pool(pool, lay)
+    H = cfg.n_kv_heads
+    mism = coords = 0
+    for l in range(cfg.n_layers):
+        kl, vl = gen_k_layer(cfg, l), gen_v_layer(cfg, l)
+        codes, scales = oracle.q8_0_encode(kl)
+        sl = slice(l * H, (l + 1) * H)
+        assert np.array_equal(got["k_codes"][sl], codes), "layer %d key codes" % l
+        assert np.array_equal(got["k_scales"][sl].view(np.uint16), scales.view(np.uint16)), l
+        vcodes, vnorms = oracle.tq_mse_encode(vl, B32)
+        m, c = check_v_codes(got["v_planes"][sl], oracle.pack_v_planes(vcodes), vl, cfg.n_tokens)
+        mism, coords = mism + m, coords + c
+        check_norms(got["v_norms"][sl], vnorms)
+    assert mism < 1e-5 * coords
+    _say("  value-code mismatches %d of %d" % (mism, coords))
+
+
+@pytest.mark.parametrize("T", [1, 31, 33, 100])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_compress_ragged_and_dims(T, d):
+    rng = np.random.default_rng(T * 1000 + d)
+    L, H = 2, 3
+    kx = (rng.standard_normal((L, H, T, d)) * rng.lognormal(0, 1, (L, H, 1, d))).astype(np.float16)
+    vx = rng.standard_normal((L, H, T, d)).astype(np.float16)
+    lay = pk.polykv_pool_layout(L, H, d, T)
+    pool = new_pool(lay)
+    pk.polykv_compress_k(torch.from_numpy(kx).to(device()), pool, lay)
+    pk.polykv_compress_v(torch.from_numpy(vx).to(device()), pool, lay)
+    got = read_pool(pool, lay)
+    codes, scales = oracle.q8_0_encode(kx)
+    assert np.array_equal(got["k_codes"], codes.reshape(L * H, T, d))
+    assert np.array_equal(got["k_scales"].view(np.uint16), scales.reshape(L * H, T, d // 32).view(np.uint16))
+    vcodes, vnorms = oracle.tq_mse_encode(vx, B32)
+    check_v_codes(got["v_planes"], oracle.pack_v_planes(vcodes).reshape(L * H, -1, 3, d),
+                  vx.reshape(L * H, T, d), T)
+    check_norms(got["v_norms"], vnorms.reshape(L * H, T))
+
+
+def test_compress_special_values():
+    d, T = 128, 64
+    kx = np.zeros((1, 1, T, d), dtype=np.float16)
+    kx[0, 0, 0, 0] = 127 / 128                                   # scale 2^-7 exactly
+    kx[0, 0, 0, 1:9] = [(2 * j + 1) / 256 for j in range(8)]     # ties k + 1/2
+    kx[0, 0, 0, 9:17] = [-(2 * j + 1) / 256 for j in range(8)]
+    kx[0, 0, 2, 0] = np.float16(178 * 2.0 ** -24)                 # subnormal scale, clamp
+    kx[0, 0, 2, 1] = np.float16(-178 * 2.0 ** -24)
+    kx[0, 0, 3, :] = 65504.0                                      # largest fp16
+    kx[0, 0, 4, :] = -0.0
+    vx = np.zeros((1, 1, T, d), dtype=np.float16)
+    vx[0, 0, 1, 5] = 3.0                                          # one-hot
+    vx[0, 0, 2, :] = 0.5                                          # constant
+    vx[0, 0, 3, :] = -2.0
+    vx[0, 0, 4, 7] = -1e-4
+    vx[0, 0, 5:, :] = np.random.default_rng(1).standard_normal((T - 5, d)).astype(np.float16)
+    lay = pk.polykv_pool_layout(1, 1, d, T)
+    pool = new_pool(lay)
+    pk.polykv_compress_k(torch.from_numpy(kx).to(device()), pool, lay)
+    pk.polykv_compress_v(torch.from_numpy(vx).to(device()), pool, lay)
+    got = read_pool(pool, lay)
+    codes, scales = oracle.q8_0_encode(kx)
+    assert np.array_equal(got["k_codes"][0], codes[0, 0])
+    assert np.array_equal(got["k_scales"][0].view(np.uint16), scales[0, 0].view(np.uint16))
+    assert list(got["k_codes"][0, 0, 1:9]) == [0, 2, 2, 4, 4, 6, 6, 8]
+    vcodes, vnorms = oracle.tq_mse_encode(vx, B32)
+    want = oracle.pack_v_planes(vcodes).reshape(1, -1, 3, d)
+    check_v_codes(got["v_planes"], want, vx.reshape(1, T, d), T)
+    # tokens 0-4 are constructed (zero, one-hot, constants): their codes admit no slack,
+    # including the zero coordinates of the constant vectors that sit on the middle boundary
+    low5 = np.uint32(0x1F)
+    assert np.array_equal(got["v_planes"][0, 0] & low5, want[0, 0] & low5)
+    assert np.array_equal(got["v_norms"][0, :5].view(np.uint16), vnorms[0, 0, :5].view(np.uint16))
+    check_norms(got["v_norms"], vnorms.reshape(1, T))
+
+
+def test_layer_range_writes_only_its_layers():
+    L, H, d, T = 3, 2, 128, 70
+    lay = pk.polykv_pool_layout(L, H, d, T)
+    rng = np.random.default_rng(3)
+    kx = rng.standard_normal((1, H, T, d)).astype(np.float16)
+    pool = new_pool(lay, fill=0x5A)
+    before = pool.clone()
+    pk.polykv_compress_k(torch.from_numpy(kx).to(device()), pool, lay, layer_begin=1, layer_count=1)
+    pk.polykv_compress_v(torch.from_numpy(kx).to(device()), pool, lay, layer_begin=1, layer_count=1)
+    got = read_pool(pool, lay)
+    old = read_pool(before, lay)
+    for name in got:
+        for t in (0, 1, 4, 5):
+            assert np.array_equal(got[name][t].view(np.uint8), old[name][t].view(np.uint8)), (name, t)
+    codes, _ = oracle.q8_0_encode(kx)
+    assert np.array_equal(got["k_codes"][2:4], codes[0])
+    # bytes outside every payload are untouched
+    flat, flat0 = pool.cpu().numpy(), before.cpu().numpy()
+    mask = np.ones(lay.total_bytes, dtype=bool)
+    G = (T + 31) // 32
+    for off, stride, n in [(lay.k_codes_off, lay.k_codes_tile_stride, T * d),
+                           (lay.k_scales_off, lay.k_scales_tile_stride, T * d // 16),
+                           (lay.v_planes_off, lay.v_planes_tile_stride, G * 3 * d * 4),
+                           (lay.v_norms_off, lay.v_norms_tile_stride, 2 * T)]:
+        for t in range(L * H):
+            mask[off + t * stride: off + t * stride + n] = False
+    assert np.array_equal(flat[mask], flat0[mask])
+
+
+def test_non_default_stream_and_determinism():
+    cfg = CONFIGS[1]
+    lay = layout_for(cfg)
+    k, v = upload_kv(cfg, layers=range(cfg.n_layers))
+    s = torch.cuda.Stream()
+    pools = []
+    for _ in range(2):
+        pool = new_pool(lay)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            pk.polykv_compress_k(k, pool, lay, stream=s)
+            pk.polykv_compress_v(v, pool, lay, stream=s)
+        pools.append(pool)
+    s.synchronize()
+    assert torch.equal(pools[0], pools[1])

@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI: exports, layout, built-in codebook, argument validation.
+
+No kernel is launched here; every call either returns before any device work or, on a
+machine without a GPU, stops at the device check.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import agent_q8_quant_amd as pk
+from agent_q8_quant_amd import polykv as B
+from oracle import analytic_pool_bytes, codebook_fp32
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from agent_q8_quant_amd.build import build
+        build()
+    return pk.lib()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "polykv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(polykv_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B.EXPORTED_SYMBOLS)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_layout(L, cfg):
+    lay = pk.polykv_pool_layout(cfg.n_layers, cfg.n_kv_heads, cfg.head_dim, cfg.n_tokens)
+    tiles, T, d = cfg.n_layers * cfg.n_kv_heads, cfg.n_tokens, cfg.head_dim
+    G = (T + 31) // 32
+    up = lambda x: (x + 255) // 256 * 256
+    assert lay.k_codes_tile_stride == up(T * d)
+    assert lay.k_scales_tile_stride == up(T * d // 16)
+    assert lay.v_planes_tile_stride == up(G * 3 * d * 4)
+    assert lay.v_norms_tile_stride == up(2 * T)
+    offs = [lay.k_codes_off, lay.k_scales_off, lay.v_planes_off, lay.v_norms_off]
+    strides = [lay.k_codes_tile_stride, lay.k_scales_tile_stride, lay.v_planes_tile_stride,
+               lay.v_norms_tile_stride]
+    assert offs[0] == 0 and all(o % 256 == 0 for o in offs)
+    for i in range(3):
+        assert offs[i + 1] == offs[i] + tiles * strides[i]
+    assert lay.total_bytes == offs[3] + tiles * strides[3]
+    assert lay.analytic_bytes == analytic_pool_bytes(cfg.n_layers, cfg.n_kv_heads, T, d)
+    # padding: at most 255 B per tile and region, plus the last token group's planes
+    pad = lay.total_bytes - lay.analytic_bytes
+    assert 0 <= pad <= tiles * (4 * 255 + (32 * G - T) * 3 * d // 8)
+
+
+def test_default_codebook_bitwise_equals_oracle(L):
+    cb = pk.polykv_codebook_default()
+    c32, b32 = codebook_fp32()
+    assert np.array_equal(np.array(cb.centroid[:], dtype=np.float32), c32)
+    assert np.array_equal(np.array(cb.boundary[:], dtype=np.float32), b32)
+
+
+def _layout(n_layers=2, H=2, d=128, T=100):
+    return pk.polykv_pool_layout(n_layers, H, d, T)
+
+
+def test_layout_errors(L):
+    out = B.polykv_layout_t()
+    for shape in [(0, 1, 128, 10), (1, 0, 128, 10), (1, 1, 128, 0), (1, 1, 32, 10), (1, 1, 96, 10)]:
+        s = B.polykv_shape_t(*shape)
+        assert L.polykv_pool_layout(ctypes.byref(s), ctypes.byref(out)) == -2
+    assert L.polykv_pool_layout(None, ctypes.byref(out)) == -1
+    with pytest.raises(pk.PolyKVError):
+        pk.polykv_pool_layout(1, 1, 48, 10)
+
+
+A16, A256 = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+
+
+def test_compress_validation(L):
+    lay = _layout()
+    lb = ctypes.byref(lay)
+    assert L.polykv_compress_k(None, A256, lb, 0, 2, None) == -1
+    assert L.polykv_compress_k(A16, None, lb, 0, 2, None) == -1
+    assert L.polykv_compress_k(A16, A256, None, 0, 2, None) == -1
+    assert L.polykv_compress_k(A16, ctypes.c_void_p(0x20010), lb, 0, 2, None) == -3
+    assert L.polykv_compress_k(ctypes.c_void_p(0x10008), A256, lb, 0, 2, None) == -3
+    assert L.polykv_compress_k(A16, A256, lb, 1, 2, None) == -4
+    assert L.polykv_compress_k(A16, A256, lb, -1, 1, None) == -4
+    assert L.polykv_compress_k(A16, A256, lb, 0, 0, None) == -4
+    bad = _layout()
+    bad.total_bytes -= 1
+    assert L.polykv_compress_k(A16, A256, ctypes.byref(bad), 0, 2, None) == -9
+    cb = pk.polykv_codebook_default()
+    cb.boundary[4] += 1e-3       # no longer symmetric
+    assert L.polykv_compress_v(A16, A256, lb, ctypes.byref(cb), 0, 2, None) == -8
+    cb = pk.polykv_codebook_default()
+    cb.centroid[0], cb.centroid[1] = cb.centroid[1], cb.centroid[0]
+    assert L.polykv_compress_v(A16, A256, lb, ctypes.byref(cb), 0, 2, None) == -8
+
+
+def _attend(L, lay, n_agents=2, gqa=2, scale=0.1, lb=0, lc=2, ws=None, wsb=0, path=0,
+            pool=A256, q=A16, out=A16, cb=None):
+    return L.polykv_attend_shared_path(pool, ctypes.byref(lay), cb, q, out, n_agents, gqa,
+                                       scale, lb, lc, ws, wsb, None, path)
+
+
+def test_attend_validation(L):
+    lay = _layout()
+    assert _attend(L, lay, pool=None) == -1
+    assert _attend(L, lay, q=None) == -1
+    assert _attend(L, lay, n_agents=0) == -2
+    assert _attend(L, lay, q=ctypes.c_void_p(0x10004)) == -3
+    assert _attend(L, lay, lb=2, lc=1) == -4
+    assert _attend(L, lay, n_agents=17, gqa=4) == -4    # 68 rows > 64
+    assert _attend(L, lay, scale=float("inf")) == -10
+    assert _attend(L, lay, path=3) == -10
+    cb = pk.polykv_codebook_default()
+    cb.boundary[3] = 1e-3
+    cb.boundary[2] = -1e-3
+    assert _attend(L, lay, cb=ctypes.byref(cb)) == -8
+
+
+def test_strerror(L):
+    for code in range(0, -11, -1):
+        assert isinstance(pk.polykv_strerror(code), str) and pk.polykv_strerror(code)
+    assert pk.polykv_strerror(-99) == "unknown error code"
+
+
+def test_device_check_without_gpu(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lay = _layout()
+    assert L.polykv_compress_k(A16, A256, ctypes.byref(lay), 0, 2, None) == -6
+    assert _attend(L, lay) == -6
+
+
+def test_binding_requires_device_tensors(L):
+    import torch
+    lay = _layout()
+    with pytest.raises(TypeError):
+        pk.polykv_compress_k(torch.zeros(2 * 2 * 100 * 128, dtype=torch.float16),
+                             torch.zeros(lay.total_bytes, dtype=torch.uint8), lay)
