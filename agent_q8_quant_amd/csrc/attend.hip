@@ -272,8 +272,4 @@ hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s) {
     }
 }
 
-bool attend_mfma_supported(const PoolGeom&, int32_t) { return false; }
-
-hipError_t launch_attend_mfma(const AttendArgs&, hipStream_t) { return hipErrorNotSupported; }
-
 }  // namespace polykv

@@ -70,7 +70,7 @@ def _traffic(kernel_key, src_names, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, n_layers_sample):
+def cpu_baseline(cfg, n_layers_sample, n_steps_sample):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
     import oracle
@@ -82,7 +82,7 @@ def cpu_baseline(cfg, n_layers_sample):
         blas_threads = 1
     c32, b32 = oracle.codebook_fp32()
     tc = td = ta = 0.0
-    q = gen_q_step(cfg, 0)
+    qs = [gen_q_step(cfg, s) for s in range(n_steps_sample)]
     for l in range(n_layers_sample):
         k, v = gen_k_layer(cfg, l), gen_v_layer(cfg, l)
         t = time.perf_counter()
@@ -91,12 +91,13 @@ def cpu_baseline(cfg, n_layers_sample):
         t = time.perf_counter()
         kh, vh = oracle.dequant_pool(pool, c32)
         td += time.perf_counter() - t
-        t = time.perf_counter()
-        oracle.shared_pool_decode(q[l:l + 1], kh[None], vh[None], cfg.gqa, cfg.softmax_scale)
-        ta += time.perf_counter() - t
-    n = n_layers_sample
+        for q in qs:
+            t = time.perf_counter()
+            oracle.shared_pool_decode(q[l:l + 1], kh[None], vh[None], cfg.gqa, cfg.softmax_scale)
+            ta += time.perf_counter() - t
+    n, ns = n_layers_sample, n_steps_sample
     L, D = cfg.n_layers, cfg.decode_steps
-    job = (tc + td) / n * L + ta / n * L * D
+    job = (tc + td) / n * L + ta / (n * ns) * L * D
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -107,8 +108,9 @@ def cpu_baseline(cfg, n_layers_sample):
         pass
     return {"value": cfg.n_agents * D / job, "unit": "agent-tokens/s",
             "cores": int(blas_threads), "kind": "oracle",
-            "sample": "%d of %d layers: oracle compress + per-token dequant once, one decode step; "
-                      "job time = L/n * (compress + dequant) + L/n * D * decode" % (n, L),
+            "sample": "%d of %d layers, %d of %d decode steps: oracle compress + per-token dequant "
+                      "of those layers, then those steps' attention; job time = L/n * (compress + "
+                      "dequant) + L*D/(n*s) * attention" % (n, L, ns, D),
             "seconds_measured": round(tc + td + ta, 2),
             "compress_GBps": (cfg.kv_elems * 4 + _analytic(cfg)) / ((tc / n) * L) / 1e9,
             "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
@@ -250,8 +252,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        n = args.cpu_sample_layers or max(1, min(cfg.n_layers, 4))
-        result["cpu_baseline"] = cpu_baseline(cfg, n)
+        n = args.cpu_sample_layers or cfg.n_layers
+        result["cpu_baseline"] = cpu_baseline(cfg, n, max(1, min(D, 8)))
     print(json.dumps(result), flush=True)
 
 

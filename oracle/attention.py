@@ -10,14 +10,18 @@ head floor(j / G) when G query heads share a KV head.
 import numpy as np
 
 
-def attention_rows(q, k_hat, v_hat, scale: float) -> np.ndarray:
-    """q [R][d], k_hat [T][d], v_hat [T][d] -> [R][d]; softmax(scale * q k^T) v in fp64."""
+def attention_weights(q, k_hat, scale: float) -> np.ndarray:
+    """q [R][d], k_hat [T][d] -> softmax(scale * q k^T) [R][T] in fp64."""
     q = np.asarray(q, dtype=np.float64)
     s = scale * (q @ np.asarray(k_hat, dtype=np.float64).T)
     s = s - np.max(s, axis=-1, keepdims=True)
     p = np.exp(s)
-    p = p / np.sum(p, axis=-1, keepdims=True)
-    return p @ np.asarray(v_hat, dtype=np.float64)
+    return p / np.sum(p, axis=-1, keepdims=True)
+
+
+def attention_rows(q, k_hat, v_hat, scale: float) -> np.ndarray:
+    """q [R][d], k_hat [T][d], v_hat [T][d] -> [R][d]; softmax(scale * q k^T) v in fp64."""
+    return attention_weights(q, k_hat, scale) @ np.asarray(v_hat, dtype=np.float64)
 
 
 def shared_pool_decode(q, k_hat, v_hat, gqa: int, scale: float, layers=None) -> np.ndarray:

@@ -12,7 +12,7 @@ import oracle
 from workloads import CONFIGS, gen_k_layer, gen_q_step, gen_v_layer
 
 from gpu_helpers import (B32, C32, DECODE_REL_TOL, device, layout_for, new_pool,
-                         pool_from_arrays, row_rel_err, upload_kv, upload_q)
+                         pool_from_arrays, read_pool, row_rel_err, upload_kv, upload_q)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _sample_steps(cfg):
     return sorted({0, cfg.decode_steps - 1})
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=5)
 def _oracle_pool(cfg):
     """The oracle's own compression of the whole workload, as [tiles][...] arrays."""
     parts = {"k_codes": [], "k_scales": [], "v_codes": [], "v_planes": [], "v_norms": []}
@@ -96,9 +96,26 @@ def test_decode_on_oracle_pool(cfg, path):
     _say("  worst row relative error %.3e" % worst)
 
 
+def _value_pool_differences(got, opool, T, d):
+    """Per (tile, token): coordinates whose value code differs, and |norm difference|."""
+    diff = np.bitwise_xor(got["v_planes"], opool["v_planes"])
+    anyp = diff[:, :, 0, :] | diff[:, :, 1, :] | diff[:, :, 2, :]      # [tiles][G][d]
+    bits = (anyp[..., None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)  # [tiles][G][d][32]
+    nflip = bits.sum(axis=2).reshape(anyp.shape[0], -1)[:, :T]         # [tiles][T]
+    dn = np.abs(got["v_norms"].astype(np.float64) - opool["v_norms"].astype(np.float64))
+    return nflip, dn
+
+
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
 def test_end_to_end(cfg):
-    """GPU compress then GPU decode, against the oracle's compress then decode."""
+    """GPU compress then GPU decode, against the oracle's compress then decode.
+
+    The two pools may legitimately differ (value codes of near-boundary coordinates, norms
+    by one fp16 ulp). A row must meet the decode tolerance plus the largest change those
+    differences can cause: for each differing token t, weight p_t (the oracle's softmax)
+    times (flipped coordinates * n_t / d * widest centroid gap + |dn_t| / n_t * max |v_t|).
+    Rows of tiles with identical pools get no allowance.
+    """
     _say("end-to-end parity", cfg.name)
     lay = layout_for(cfg)
     k, v = upload_kv(cfg)
@@ -107,26 +124,53 @@ def test_end_to_end(cfg):
     pk.polykv_compress_v(v, pool, lay)
     del k, v
     opool = _oracle_pool(cfg)
+    got = read_pool(pool, lay)
+    assert np.array_equal(got["k_codes"], opool["k_codes"].reshape(got["k_codes"].shape))
+    nflip, dn = _value_pool_differences(got, opool, cfg.n_tokens, cfg.head_dim)
+    gap = float(np.max(np.diff(C32.astype(np.float64))))
     layers = _sample_layers(cfg)
     step = cfg.decode_steps - 1
     qn = gen_q_step(cfg, step)
     q = torch.from_numpy(qn).to(device())
     out = torch.empty_like(q)
     pk.polykv_attend_shared(pool, lay, q, out, cfg.n_agents, cfg.gqa, cfg.softmax_scale)
-    err = row_rel_err(out.cpu().numpy()[layers], _oracle_decode(cfg, opool, qn, layers))
-    _say("  worst row relative error %.3e" % err)
-    assert err <= DECODE_REL_TOL
+    o = out.cpu().numpy().astype(np.float64)
+    H, G, A, d = cfg.n_kv_heads, cfg.gqa, cfg.n_agents, cfg.head_dim
+    worst_strict, n_allowed = 0.0, 0
+    for l in layers:
+        for h in range(H):
+            t = l * H + h
+            kh, vh = oracle.dequant_pool({"k_codes": opool["k_codes"][t], "k_scales": opool["k_scales"][t],
+                                          "v_codes": opool["v_codes"][t], "v_norms": opool["v_norms"][t]}, C32)
+            rows = qn[l, :, h * G:(h + 1) * G, :].reshape(A * G, d)
+            w = oracle.attention_weights(rows, kh, cfg.softmax_scale)
+            ref = w @ vh
+            n = np.maximum(opool["v_norms"][t].astype(np.float64), got["v_norms"][t].astype(np.float64))
+            per_tok = nflip[t] * n / d * gap + dn[t] / np.maximum(n, 1e-30) * np.max(np.abs(vh), axis=-1)
+            allow = w @ per_tok
+            err = np.max(np.abs(o[l, :, h * G:(h + 1) * G, :].reshape(A * G, d) - ref), axis=-1)
+            scale = np.max(np.abs(ref), axis=-1)
+            assert np.all(err <= DECODE_REL_TOL * scale + allow * 1.0001), (l, h, np.max(err / scale))
+            strict = allow == 0
+            n_allowed += int(np.count_nonzero(~strict))
+            if np.any(strict):
+                worst_strict = max(worst_strict, float(np.max(err[strict] / scale[strict])))
+    _say("  rows with an allowance %d; worst error elsewhere %.3e; tokens with a differing value %d"
+         % (n_allowed, worst_strict, int(np.count_nonzero(nflip) + np.count_nonzero(dn))))
 
 
 def _tiny_pool(T, d=128, H=2, L=1, seed=0, v_override=None):
+    """The oracle's pool of seeded inputs, uploaded as the library's byte image, so that the
+    decode is compared on exactly the pool the oracle reads."""
     rng = np.random.default_rng(seed)
     kx = rng.standard_normal((L, H, T, d)).astype(np.float16)
     vx = rng.standard_normal((L, H, T, d)).astype(np.float16) if v_override is None else v_override
     lay = pk.polykv_pool_layout(L, H, d, T)
-    pool = new_pool(lay)
-    pk.polykv_compress_k(torch.from_numpy(kx).to(device()), pool, lay)
-    pk.polykv_compress_v(torch.from_numpy(vx).to(device()), pool, lay)
     op = oracle.compress_pool(kx, vx, B32)
+    tiles = L * H
+    img = pool_from_arrays(lay, op["k_codes"].reshape(tiles, T, d), op["k_scales"].reshape(tiles, T, d // 32),
+                           op["v_planes"].reshape(tiles, -1, 3, d), op["v_norms"].reshape(tiles, T))
+    pool = torch.from_numpy(img).to(device())
     kh, vh = oracle.dequant_pool(op, C32)
     return lay, pool, kh, vh
 
@@ -154,9 +198,11 @@ def test_ragged_tokens_and_rows(T, rows, path):
 
 
 @pytest.mark.parametrize("path", PATHS, ids=["valu", "mfma"])
-@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_head_dims(d, path):
     _supported(path, CONFIGS[0])
+    if path == pk.POLYKV_PATH_MFMA and d == 256:
+        pytest.skip("the matrix-core path covers head_dim 64 and 128")
     lay, pool, kh, vh = _tiny_pool(300, d=d, H=3, L=2, seed=d)
     A, G = 3, 2
     qn = np.random.default_rng(d).standard_normal((2, A, 3 * G, d)).astype(np.float32)

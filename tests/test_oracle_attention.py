@@ -5,7 +5,8 @@ import math
 import numpy as np
 import pytest
 
-from oracle import attention_rows, codebook_fp32, compress_pool, dequant_pool, shared_pool_decode
+from oracle import (attention_rows, attention_weights, codebook_fp32, compress_pool, dequant_pool,
+                    shared_pool_decode)
 
 
 def _brute(q, k, v, scale):
@@ -65,3 +66,14 @@ def test_agent_permutation_and_gqa_head_mapping():
     for j in range(H * G):
         want = attention_rows(q[1, :, j, :], kh[1, j // G], vh[1, j // G], 0.125)
         assert np.allclose(o[1, :, j, :], want, atol=1e-14)
+
+
+def test_weights_brute_force_and_normalised():
+    rng = np.random.default_rng(8)
+    q, k = rng.standard_normal((3, 16)), rng.standard_normal((6, 16))
+    w = attention_weights(q, k, 0.3)
+    assert np.allclose(w.sum(axis=-1), 1.0, atol=1e-15)
+    for r in range(3):
+        s = [0.3 * sum(float(a) * float(b) for a, b in zip(q[r], kt)) for kt in k]
+        e = [math.exp(x - max(s)) for x in s]
+        assert np.allclose(w[r], [x / sum(e) for x in e], atol=1e-15)
