@@ -107,10 +107,45 @@ bool codebook_ok(const polykv_codebook_t& cb) {
     return cb.boundary[3] == 0.0f;
 }
 
+// Scale lambda in [1, 2) (steps of 2^-16) minimising the worst relative fp16 rounding
+// error of lambda * c over the four positive centroids.
+float fp16_friendly_scale(const float* c) {
+    float best_lam = 1.0f;
+    double best_err = 1e30;
+    for (int i = 0; i < 65536; ++i) {
+        const float lam = 1.0f + (float)i / 65536.0f;
+        double err = 0.0;
+        for (int k = 0; k < 4; ++k) {
+            const float v = lam * c[k];
+            const double h = (double)(float)(_Float16)v;
+            err = std::fmax(err, std::fabs(h - (double)v) / (double)v);
+        }
+        if (err < best_err) {
+            best_err = err;
+            best_lam = lam;
+        }
+    }
+    return best_lam;
+}
+
 polykv::CodebookHalf half_of(const polykv_codebook_t& cb) {
     polykv::CodebookHalf h;
     for (int k = 0; k < 4; ++k) h.centroid_pos[k] = cb.centroid[4 + k];
     for (int k = 0; k < 3; ++k) h.boundary_pos[k] = cb.boundary[4 + k];
+    // the default codebook's scale is computed once; another codebook's is cached per
+    // thread for as long as the same codebook keeps being passed
+    static const float default_scale = fp16_friendly_scale(&default_codebook().centroid[4]);
+    if (std::memcmp(&cb, &default_codebook(), sizeof(cb)) == 0) {
+        h.fp16_scale = default_scale;
+    } else {
+        thread_local polykv_codebook_t last_cb;
+        thread_local float last_scale = 0.0f;
+        if (last_scale == 0.0f || std::memcmp(&cb, &last_cb, sizeof(cb)) != 0) {
+            last_scale = fp16_friendly_scale(h.centroid_pos);
+            last_cb = cb;
+        }
+        h.fp16_scale = last_scale;
+    }
     return h;
 }
 

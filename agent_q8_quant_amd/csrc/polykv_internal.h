@@ -38,6 +38,10 @@ inline PoolGeom make_geom(const polykv_layout_t& l) {
 struct CodebookHalf {
     float centroid_pos[4];   // centroid[4..7]
     float boundary_pos[3];   // boundary[4..6]; boundary[3] is 0
+    // lambda in [1, 2) for which the fp16 roundings of lambda * centroid_pos[k] have the
+    // smallest worst relative error; kernels that hold centroids in fp16 store
+    // lambda * c and divide the result by lambda
+    float fp16_scale;
 };
 
 // Kernel launchers (defined in compress.hip / attend.hip). They return hipError_t of the
