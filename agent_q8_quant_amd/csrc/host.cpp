@@ -245,6 +245,16 @@ static int resolve_path(const polykv::PoolGeom& g, int32_t rows, int32_t path) {
     return path;
 }
 
+int polykv_attend_path(const polykv_layout_t* layout, int32_t n_agents, int32_t gqa) {
+    if (!layout) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (n_agents < 1 || gqa < 1) return POLYKV_ERR_SHAPE;
+    if ((int64_t)n_agents * gqa > POLYKV_MAX_ROWS) return POLYKV_ERR_RANGE;
+    polykv::PoolGeom g = polykv::make_geom(*layout);
+    return resolve_path(g, n_agents * gqa, POLYKV_PATH_AUTO);
+}
+
 size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_agents,
                                      int32_t gqa, int32_t layer_count) {
     if (!layout || check_layout(layout) != POLYKV_OK || n_agents < 1 || gqa < 1 || layer_count < 1)

@@ -19,7 +19,7 @@ POLYKV_MAX_ROWS = 64
 
 EXPORTED_SYMBOLS = (
     "polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k", "polykv_compress_v",
-    "polykv_attend_workspace_bytes", "polykv_attend_shared", "polykv_attend_shared_path",
+    "polykv_attend_workspace_bytes", "polykv_attend_path", "polykv_attend_shared", "polykv_attend_shared_path",
     "polykv_strerror",
 )
 
@@ -66,6 +66,8 @@ def lib():
                                         ctypes.POINTER(polykv_codebook_t), i32, i32, vp]
         L.polykv_attend_workspace_bytes.argtypes = [ctypes.POINTER(polykv_layout_t), i32, i32, i32]
         L.polykv_attend_workspace_bytes.restype = sz
+        L.polykv_attend_path.argtypes = [ctypes.POINTER(polykv_layout_t), i32, i32]
+        L.polykv_attend_path.restype = ctypes.c_int
         att = [vp, ctypes.POINTER(polykv_layout_t), ctypes.POINTER(polykv_codebook_t), vp, vp,
                i32, i32, ctypes.c_float, i32, i32, vp, sz, vp]
         L.polykv_attend_shared.argtypes = att
@@ -148,6 +150,12 @@ def polykv_compress_v(v, pool, layout, cb=None, layer_begin=0, layer_count=None,
 def polykv_attend_workspace_bytes(layout, n_agents, gqa, layer_count=None) -> int:
     _, lc = _layers(layout, 0, layer_count)
     return int(lib().polykv_attend_workspace_bytes(ctypes.byref(layout), n_agents, gqa, lc))
+
+
+def polykv_attend_path(layout, n_agents, gqa) -> int:
+    rc = int(lib().polykv_attend_path(ctypes.byref(layout), int(n_agents), int(gqa)))
+    _check(min(rc, 0), "polykv_attend_path")
+    return rc
 
 
 def polykv_attend_shared_path(pool, layout, q, out, n_agents, gqa, softmax_scale, path,

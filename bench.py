@@ -5,9 +5,12 @@ compression of the fp16 K and V of every layer into the pool (compress_k + compr
 then D decode steps of all agents against that pool (one attend_shared launch each).
 Inputs (fp16 K/V and the queries of all D decode steps) are resident in HBM before timing.
 
-Each kernel launch is timed with HIP events on the launch stream. Before every timed launch
-a 1 GiB buffer is read and written outside the events, which evicts the 256 MB Infinity
-Cache, so that the pool really comes from HBM (the default; --warm skips it).
+Every launch goes to one explicit stream and is bracketed by HIP events recorded on that
+stream. Three identical copies of the pool are used in turn, so each decode launch reads a
+copy that at least two pool-sized streams have passed through the 256 MB Infinity Cache
+since it was last touched: it comes from HBM (--warm uses a single copy). Decode launches
+right after a 1 GiB write (cold caches and address translations) are timed separately and
+reported beside the main figures.
 
 Prints ONE JSON line. value = whole-job agent-tokens/s = agents * D / (compress time +
 D * decode time), from the event times. Also reported: compress GB/s and decode GB/s over
@@ -38,7 +41,7 @@ def _parse():
     p.add_argument("--config", default="3", help="workload index or name (default: the 4K Llama-3-8B pool)")
     p.add_argument("--decode-steps", type=int, default=None, help="decode launches per step (default: the workload's)")
     p.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
-    p.add_argument("--warm", action="store_true", help="do not evict the Infinity Cache between launches")
+    p.add_argument("--warm", action="store_true", help="one pool copy, left in the caches between launches")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-layers", type=int, default=None)
     p.add_argument("--mode", choices=["bench", "profile", "copy"], default="bench",
@@ -55,19 +58,18 @@ def _src_sha(names):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_key, src_names, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _traffic(kernel, src_names, workload):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    try:
-        rec = json.load(open(path)).get(kernel_key, {}).get(workload)
-    except (ValueError, AttributeError):
-        return None
-    if not rec or rec.get("source_sha") != _src_sha(src_names):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    sha = _src_sha(src_names)
+    for line in open(path):
+        f = line.split()
+        if len(f) == 4 and not line.startswith("#") and f[0] == kernel and f[1] == workload:
+            return int(f[3]) if f[2] == sha else None
+    return None
 
 
 def cpu_baseline(cfg, n_layers_sample, n_steps_sample):
@@ -163,56 +165,80 @@ def main():
     for s in range(D):
         q[s].copy_(torch.from_numpy(gen_q_step(cfg, s)))
     out = torch.empty(qshape, dtype=torch.float32, device=dev)
-    pool = torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev)
     ws_bytes = pk.polykv_attend_workspace_bytes(lay, cfg.n_agents, cfg.gqa)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if not args.warm else None
+    n_pools = 1 if args.warm else 3
+    pools = [torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev) for _ in range(n_pools)]
+    stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
-    def evict():
-        if flush is not None:
-            flush.add_(1)
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
 
-    def timed(fn, ev_list):
-        evict()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fn()
-        e1.record()
-        ev_list.append((e0, e1))
+    def decode(p, s):
+        pk.polykv_attend_shared_path(pools[p], lay, q[s], out, cfg.n_agents, cfg.gqa,
+                                     cfg.softmax_scale, path, workspace=ws, stream=stream)
 
-    def one_step(rec):
-        timed(lambda: pk.polykv_compress_k(k, pool, lay), rec["ck"])
-        timed(lambda: pk.polykv_compress_v(v, pool, lay), rec["cv"])
+    def one_step(j, rec):
+        # The step compresses into pool j % n and decodes from the others in turn, so each
+        # decode launch reads a pool that at least two pool-sized reads have passed since
+        # (nothing of it is left in the 256 MB Infinity Cache); all copies are identical.
+        pw = j % n_pools
+        e = [ev()]
+        pk.polykv_compress_k(k, pools[pw], lay, stream=stream)
+        e.append(ev())
+        pk.polykv_compress_v(v, pools[pw], lay, stream=stream)
+        e.append(ev())
         for s in range(D):
-            timed(lambda: pk.polykv_attend_shared_path(pool, lay, q[s], out, cfg.n_agents, cfg.gqa,
-                                                       cfg.softmax_scale, path, workspace=ws), rec["at"])
+            decode((pw + 1 + s) % n_pools, s)
+            e.append(ev())
+        rec.append(e)
 
-    if args.mode == "profile":
-        rec = {"ck": [], "cv": [], "at": []}
-        for _ in range(max(1, args.steps)):
-            one_step(rec)
+    with torch.cuda.stream(stream):
+        if args.mode == "profile":
+            for j in range(n_pools + max(1, args.steps)):
+                one_step(j, [])
+            stream.synchronize()
+            print("profile run done: %d steps x (2 compress + %d decode) launches"
+                  % (n_pools + args.steps, D), flush=True)
+            return
+        for j in range(max(args.warmup, n_pools)):  # every pool copy written before timing
+            one_step(j, [])
+        stream.synchronize()
+        print("bench: warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
+        rec = []
         torch.cuda.synchronize()
-        print("profile run done: %d steps x (2 compress + %d decode) launches" % (args.steps, D), flush=True)
-        return
+        w0 = time.perf_counter()
+        for j in range(args.steps):
+            one_step(j, rec)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
 
-    for _ in range(args.warmup):
-        one_step({"ck": [], "cv": [], "at": []})
-    torch.cuda.synchronize()
-    print("bench: warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    rec = {"ck": [], "cv": [], "at": []}
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_step(rec)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
+        # Secondary figure: decode right after a 1 GiB write (cold caches and translations).
+        cold_us = []
+        if not args.warm:
+            flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            for s in range(4):
+                flush.add_(1)
+                e0 = ev()
+                decode(0, s)
+                e1 = ev()
+                cold_us.append((e0, e1))
+            stream.synchronize()
+            cold_us = [a.elapsed_time(b) * 1e3 for a, b in cold_us]
+            del flush
 
-    ms = {key: [a.elapsed_time(b) for a, b in rec[key]] for key in rec}
-    t_ck = sum(ms["ck"]) / len(ms["ck"]) / 1e3
-    t_cv = sum(ms["cv"]) / len(ms["cv"]) / 1e3
-    t_at = sum(ms["at"]) / len(ms["at"]) / 1e3
-    step_s = t_ck + t_cv + D * t_at
+    step_ms = [r[0].elapsed_time(r[-1]) for r in rec]
+    ck_ms = [r[0].elapsed_time(r[1]) for r in rec]
+    cv_ms = [r[1].elapsed_time(r[2]) for r in rec]
+    at_ms = [r[i].elapsed_time(r[i + 1]) for r in rec for i in range(2, 2 + D)]
+    step_s = sum(step_ms) / len(step_ms) / 1e3
+    t_ck = sum(ck_ms) / len(ck_ms) / 1e3
+    t_cv = sum(cv_ms) / len(cv_ms) / 1e3
+    t_at = sum(at_ms) / len(at_ms) / 1e3
 
     analytic = lay.analytic_bytes
     fp16_bytes = cfg.kv_elems * 2
@@ -222,7 +248,10 @@ def main():
     compress_gbps = compress_bytes / (t_ck + t_cv) / 1e9
     decode_gbps = decode_bytes / t_at / 1e9
     workload = cfg.name
-    traffic = _traffic("attend", ["attend.hip"], workload)
+    chosen = pk.polykv_attend_path(lay, cfg.n_agents, cfg.gqa) if path == pk.POLYKV_PATH_AUTO else path
+    kname, ksrc = (("attend_mfma", "attend_mfma.hip") if chosen == pk.POLYKV_PATH_MFMA
+                   else ("attend_valu", "attend.hip"))
+    traffic = _traffic(kname, [ksrc], workload)
     result = {
         "metric": METRIC,
         "value": cfg.n_agents * D / step_s,
@@ -230,14 +259,16 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": step_s * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8+u3 pool; fp32 accumulate" + (" (fp16 MFMA operands)" if path == pk.POLYKV_PATH_MFMA else ""),
+        "dtype": "int8+u3 pool; fp32 accumulate" + (" (fp16 MFMA operands)" if chosen == pk.POLYKV_PATH_MFMA else ""),
         "data": "synthetic",
         "config": {"workload": workload, "layers": cfg.n_layers, "kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "tokens": cfg.n_tokens, "agents": cfg.n_agents,
                    "gqa": cfg.gqa, "decode_steps": D, "v_dist": cfg.v_dist,
-                   "cache": "warm" if args.warm else "infinity-cache evicted before each launch",
-                   "path": args.path},
-        "roofline": {"kernel": "attend_shared", "bound": "hbm", "achieved": decode_gbps,
+                   "cache": ("warm: one pool copy" if args.warm else
+                             "3 identical pool copies used in turn: each decode reads a copy that "
+                             ">= 2 pool-sized reads have passed since (not in the Infinity Cache)"),
+                   "path": kname},
+        "roofline": {"kernel": kname, "bound": "hbm", "achieved": decode_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": decode_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": decode_bytes,
                      "avg_launch_us": t_at * 1e6},
@@ -250,10 +281,12 @@ def main():
                             + cfg.n_layers * cfg.n_kv_heads * cfg.n_tokens * 2) / t_cv / 1e9,
         "wall_ms_per_step": wall / args.steps * 1e3,
     }
+    if cold_us:
+        result["decode_us_after_1GiB_write"] = cold_us
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         n = args.cpu_sample_layers or cfg.n_layers
-        result["cpu_baseline"] = cpu_baseline(cfg, n, max(1, min(D, 8)))
+        result["cpu_baseline"] = cpu_baseline(cfg, n, max(1, min(D, 32)))
     print(json.dumps(result), flush=True)
 
 

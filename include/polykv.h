@@ -136,6 +136,10 @@ int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* lay
 #define POLYKV_PATH_VALU 1   /* fp32 vector-ALU contraction                               */
 #define POLYKV_PATH_MFMA 2   /* matrix-core contraction (fp16 operands, fp32 accumulate)  */
 
+/* The decode kernel POLYKV_PATH_AUTO selects for these arguments (POLYKV_PATH_VALU or
+ * POLYKV_PATH_MFMA), or a negative error code (NULL, SHAPE, RANGE, LAYOUT). Host only. */
+int polykv_attend_path(const polykv_layout_t* layout, int32_t n_agents, int32_t gqa);
+
 /* Device bytes of workspace polykv_attend_shared needs for these arguments (0 if none). */
 size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_agents,
                                      int32_t gqa, int32_t layer_count);

@@ -132,6 +132,23 @@ def test_attend_validation(L):
     assert _attend(L, lay, cb=ctypes.byref(cb)) == -8
 
 
+def test_attend_path_choice(L):
+    """The automatic choice: matrix cores for more than one 16-row MFMA tile of query rows
+    at head_dim 64/128, the vector-ALU kernel otherwise."""
+    for d, rows, want in ((128, 60, pk.POLYKV_PATH_MFMA), (64, 17, pk.POLYKV_PATH_MFMA),
+                          (128, 16, pk.POLYKV_PATH_VALU), (128, 1, pk.POLYKV_PATH_VALU),
+                          (256, 60, pk.POLYKV_PATH_VALU)):
+        lay = pk.polykv_pool_layout(2, 2, d, 100)
+        assert pk.polykv_attend_path(lay, rows, 1) == want, (d, rows)
+    lay = _layout()
+    assert L.polykv_attend_path(None, 1, 1) == -1
+    assert L.polykv_attend_path(ctypes.byref(lay), 0, 1) == -2
+    assert L.polykv_attend_path(ctypes.byref(lay), 17, 4) == -4
+    bad = pk.polykv_pool_layout(2, 2, 128, 100)
+    bad.k_codes_off += 16
+    assert L.polykv_attend_path(ctypes.byref(bad), 1, 1) == -9
+
+
 def test_strerror(L):
     for code in range(0, -11, -1):
         assert isinstance(pk.polykv_strerror(code), str) and pk.polykv_strerror(code)
