@@ -1,7 +1,6 @@
 // Shared-pool decode attention, fp32 vector-ALU path (gfx950).
 //
-// PolyKV abstract: N agents read one compressed pool ("multi-reader concurrent agent
-// access"). For a pool tile (layer, KV head) every agent's query rows of that KV head are
+// PolyKV abstract: N agents read one compressed pool concurrently. For a pool tile (layer, KV head) every agent's query rows of that KV head are
 // scored against every pool token: S = scale * q . (code * s), an online softmax runs over
 // token chunks, and P.V is accumulated in the Hadamard-rotated domain as
 // acc = sum_t p_t * n_t * c[code_t]; each output row is H acc / (d * l) with a single

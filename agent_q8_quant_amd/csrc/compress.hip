@@ -1,6 +1,6 @@
 // Write-once compression of fp16 K and V into the shared pool (gfx950).
 //
-// Keys, q8_0 (PolyKV abstract: "Keys are quantized at int8 (q8_0)"): blocks of 32 along
+// Keys, q8_0 (PolyKV abstract: keys at int8, q8_0 format): blocks of 32 along
 // head_dim, fp16 scale RNE16(amax/127), codes RNE(x/s) clamped to [-127, 127].
 // Values, TurboQuant MSE (PolyKV abstract: FWHT rotation, then 3-bit Lloyd-Max codes for
 // N(0,1)): y = H v / ||v||, code = #{k : y > b_k}, stored as three bit-planes over groups

@@ -1,7 +1,7 @@
 """Decode attention of N agents against the shared pool, in fp64.
 
-PolyKV, Abstract: the compressed pool is injected into "N independent agent contexts"
-and read with "multi-reader concurrent agent access". One decode step of one agent is
+PolyKV, Abstract: one compressed pool is handed to N separate agent contexts, all of
+which read it at the same time. One decode step of one agent is
 ordinary softmax attention of each of its query heads over every token of the shared
 pool (all pool tokens precede the query, so there is no mask). Query head j reads KV
 head floor(j / G) when G query heads share a KV head.

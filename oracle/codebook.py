@@ -1,7 +1,7 @@
 """3-bit Lloyd-Max codebook for N(0,1).
 
-PolyKV, Abstract: values are quantised with "3-bit Lloyd-Max quantization with
-centroids tuned to N(0,1)". Lloyd's method (Lloyd 1957/1982; Max 1960) alternates two
+PolyKV, Abstract: after the rotation, values get 3-bit Lloyd-Max codes whose centroids
+are fitted to the standard normal distribution. Lloyd's method (Lloyd 1957/1982; Max 1960) alternates two
 optimality conditions until a fixed point:
 - each boundary is the midpoint of its two neighbouring centroids;
 - each centroid is the mean of N(0,1) restricted to its cell.

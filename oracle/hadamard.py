@@ -1,6 +1,7 @@
 """Walsh-Hadamard transform in natural (Sylvester) order.
 
-PolyKV, Abstract: values are rotated with a "Fast Walsh-Hadamard Transform (FWHT)".
+PolyKV, Abstract: values pass through a fast Walsh-Hadamard rotation before they are
+quantised.
 The pages name no ordering, normalisation or random signs, so the plain reading is
 used: the Sylvester matrix H with H[i][j] = (-1)^popcount(i & j), no sign
 randomisation and no permutation. The orthonormal transform is H / sqrt(d).

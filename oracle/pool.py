@@ -1,7 +1,7 @@
 """The shared compressed pool: value bit-plane layout, byte counts, whole-pool helpers.
 
-PolyKV, Abstract: the system "writes a compressed cache once" and every agent reads that
-single pool. The pages fix no byte layout; the one used here:
+PolyKV, Abstract: the compressed cache is produced a single time and every agent reads
+that one pool. The pages fix no byte layout; the one used here:
 - key codes int8 [L][H][T][d] and key scales fp16 [L][H][T][d/32];
 - value codes as three bit-planes over groups of 32 tokens: uint32 words
   [L][H][ceil(T/32)][3][d]; bit j of word (g, p, i) is bit p of the code of token

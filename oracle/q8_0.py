@@ -1,6 +1,7 @@
 """q8_0 key quantisation.
 
-PolyKV, Abstract: "Keys are quantized at int8 (q8_0) to preserve softmax stability".
+PolyKV, Abstract: keys are kept at int8 in the q8_0 format, chosen there so that the
+softmax stays stable.
 Definition used (the pages fix nothing finer):
 - blocks of 32 consecutive entries along head_dim;
 - scale s = fp16(amax / 127), with amax the block's largest |x| in float32, the

@@ -1,8 +1,8 @@
 """TurboQuant-MSE value compression.
 
-PolyKV, Abstract: "Values are compressed using TurboQuant MSE -- a Fast
-Walsh-Hadamard Transform (FWHT) rotation followed by 3-bit Lloyd-Max quantization with
-centroids tuned to N(0,1)". Steps used, per value head vector v of length d:
+PolyKV, Abstract: values are compressed with TurboQuant MSE, which rotates each vector
+with a fast Walsh-Hadamard transform and then applies a 3-bit Lloyd-Max quantiser
+fitted to N(0,1). Steps used, per value head vector v of length d:
 1. n = ||v||_2;
 2. u = v / n * sqrt(d) (so the coordinates of the rotated vector are ~N(0,1));
 3. y = H u / sqrt(d), the orthonormal Sylvester FWHT;
