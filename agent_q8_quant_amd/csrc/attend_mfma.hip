@@ -7,25 +7,30 @@
 // domain, acc = sum_t p_t n_t c[code_t]; one inverse FWHT per output row at the end
 // replaces the per-token inverse rotation.
 //
-// Layout of the work (one workgroup of 8 waves per tile):
-// - the tile's tokens are cut into 32-token chunks (one value bit-plane group each); pair
-//   p of waves (p = 0..3, sharing SIMD p) takes chunks p, p+4, p+8, ...;
-// - in each pair, a score wave streams keys, block scales and norms into its LDS ring
-//   (direct-to-LDS DMA), computes S with v_mfma_f32_16x16x32_f16 (16 tokens x one
-//   32-wide q8 block as A, codes converted to fp16 exactly; 16 query rows as B, the query
-//   split q = q_hi + q_lo in fp16 for ~22-bit precision), applies the block scales with
-//   v_fma_mix, runs a lazy-max online softmax in base 2 and writes p * n_t as fp16 to a
-//   double-buffered LDS slot; a value wave streams the value bit-planes, decodes them to
+// Layout of the work (one workgroup per tile, four token streams, one per SIMD):
+// - the tile's tokens are cut into 32-token chunks (one value bit-plane group each);
+//   stream s takes chunks s, s+4, s+8, ...;
+// - each stream has score waves and two value waves, all on the stream's SIMD. A score
+//   wave owns a block of query rows: it computes S for its rows with
+//   v_mfma_f32_16x16x32_f16 (16 tokens x one 32-wide q8 block as A, codes converted to
+//   fp16 exactly; 16 query rows as B, the query split q = q_hi + q_lo in fp16 for ~22-bit
+//   precision), applies the block scales with v_fma_mix, runs a lazy-max online softmax
+//   in base 2 and writes p * n_t as fp16 to a double-buffered LDS slot. A value wave owns
+//   half of the head dimensions: it decodes the value bit-planes of its dimensions to
 //   fp16 centroids through a 4096-entry table (one nibble of each plane = 4 tokens) and
-//   accumulates P.V in fp32 one chunk behind the score wave. The two waves of a pair sit
-//   on one SIMD, so the matrix work of one overlaps the vector work of the other;
+//   accumulates P.V for every row in fp32, one chunk behind the score waves. Four waves
+//   of similar register size per SIMD hide each other's latencies;
+// - the first score wave of a stream streams the keys, block scales and norms of its
+//   chunks into an LDS ring by direct-to-LDS DMA; each value wave streams its half of
+//   the planes. One workgroup barrier per chunk step publishes keys and probabilities;
 // - a row's reference maximum is raised only when a score exceeds it by more than 8
-//   (log2 units); the score wave then passes per-row rescale factors to the value wave;
-// - at the end the pairs' (m, l, acc) are merged through LDS and each row becomes
+//   (log2 units); the score wave then passes per-row rescale factors to the value waves;
+// - at the end the streams' (m, l, acc) are merged through LDS and each row becomes
 //   H acc / (d l).
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
+
 
 #include "polykv_internal.h"
 
@@ -35,56 +40,65 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-constexpr int PAIRS = 4;
+constexpr int STREAMS = 4;
 constexpr int CHUNK = 32;
 constexpr int NSTAGE = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.0f;  // log2 units a score may exceed the reference maximum
 
-template <int D, int NRB>
+constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// D: head_dim; SRB: 16-row blocks per score wave; NSW: score waves per stream.
+template <int D, int SRB, int NSW>
 struct MCfg {
     static constexpr int NB = D / 32;                  // q8 blocks per row
-    static constexpr int NDB = D / 16;                 // 16-wide dimension blocks
-    static constexpr int SLOTS = D / 16;               // 16-byte slots in a key row
+    static constexpr int NRB = SRB * NSW;              // 16-row blocks per tile
     static constexpr int ROWS = 16 * NRB;
-    // score-wave stage: key codes, block scales, value norms
+    static constexpr int WAVES = STREAMS * (NSW + 2);
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int SLOTS = D / 16;               // 16-byte slots in a key row
+    static constexpr int HD = D / 2;                   // dimensions per value wave
+    static constexpr int VDB = HD / 16;                // 16-column blocks per value wave
+    // key stage: key codes (rows XOR-swizzled by 16-byte slot), block scales, value norms
     static constexpr int K_BYTES = CHUNK * D;
     static constexpr int S_BYTES = CHUNK * NB * 2;
     static constexpr int N_BYTES = CHUNK * 2;
-    static constexpr int A_OFF_K = 0;
     static constexpr int A_OFF_S = K_BYTES;
     static constexpr int A_OFF_N = A_OFF_S + S_BYTES;
-    static constexpr int A_STAGE = (A_OFF_N + N_BYTES + 255) / 256 * 256;
-    // value-wave stage: the three bit-planes of the chunk
-    static constexpr int V_BYTES = 3 * D * 4;
-    static constexpr int B_STAGE = (V_BYTES + 255) / 256 * 256;
-    // probabilities p * n (fp16 A operand of P.V), per row block one h8 per lane, and the
-    // per-row rescale factors with a flag
+    static constexpr int A_STAGE = round_up(A_OFF_N + N_BYTES, 256);
+    // plane stage: [value wave][plane][HD] words
+    static constexpr int VH_BYTES = 3 * HD * 4;
+    static constexpr int V_LANES = VH_BYTES / 16;      // lanes of the one DMA instruction
+    static constexpr int LPP = HD * 4 / 16;            // lanes per plane
+    static constexpr int B_STAGE = round_up(2 * VH_BYTES, 256);
+    // probabilities p * n (fp16 A operand of P.V, one h8 per lane and row block) and the
+    // per-row rescale factors, then one flag per score wave
     static constexpr int P_BYTES = NRB * 64 * 16;
-    static constexpr int ALPHA_BYTES = ROWS * 4 + 16;
-    // per pair
-    static constexpr int PAIR_OFF_A = 0;
-    static constexpr int PAIR_OFF_B = PAIR_OFF_A + NSTAGE * A_STAGE;
-    static constexpr int PAIR_OFF_P = PAIR_OFF_B + NSTAGE * B_STAGE;
-    static constexpr int PAIR_OFF_AL = PAIR_OFF_P + 2 * P_BYTES;
-    static constexpr int PAIR_BYTES = (PAIR_OFF_AL + 2 * ALPHA_BYTES + 255) / 256 * 256;
+    static constexpr int AL_STRIDE = ROWS + 4;
+    static constexpr int ST_OFF_A = 0;
+    static constexpr int ST_OFF_B = ST_OFF_A + NSTAGE * A_STAGE;
+    static constexpr int ST_OFF_P = ST_OFF_B + NSTAGE * B_STAGE;
+    static constexpr int ST_OFF_AL = ST_OFF_P + 2 * P_BYTES;
+    static constexpr int STREAM_BYTES = round_up(ST_OFF_AL + 2 * AL_STRIDE * 4, 256);
     static constexpr int LUT_BYTES = 4096 * 8;
     static constexpr int OFF_LUT = 0;
-    static constexpr int OFF_PAIRS = LUT_BYTES;
-    static constexpr int LDS = OFF_PAIRS + PAIRS * PAIR_BYTES;
+    static constexpr int OFF_MASK = LUT_BYTES;                 // fp16 [2][CHUNK] token weights
+    static constexpr int OFF_STREAMS = OFF_MASK + 256;
+    static constexpr int LDS = OFF_STREAMS + STREAMS * STREAM_BYTES;
     // DMA instructions per chunk
     static constexpr int K_INSTR = K_BYTES / 1024;
     static constexpr int S_LANES = S_BYTES / 4;
     static constexpr int A_LOADS = K_INSTR + 2;
-    static constexpr int V_INSTR = (V_BYTES + 1023) / 1024;
-    static constexpr int V_TAIL_LANES = (V_BYTES % 1024) / 16;
-    static constexpr int B_LOADS = V_INSTR;
-    // merge area (reuses the pair area at the end)
-    static constexpr int MERGE_BYTES = (2 * PAIRS * ROWS + 2 * ROWS * D) * 4;
+    // merge area (reuses the stream areas at the end)
+    static constexpr int MERGE_BYTES = (2 * STREAMS * ROWS + 2 * ROWS * D) * 4;
     static_assert(K_BYTES % 1024 == 0, "key stage is whole DMA instructions");
-    static_assert(S_LANES <= 64, "scales fit one dword DMA");
-    static_assert(MERGE_BYTES <= PAIRS * PAIR_BYTES, "merge area fits");
+    static_assert(S_LANES <= 64 && V_LANES <= 64, "one DMA instruction each");
+    static_assert(MERGE_BYTES <= STREAMS * STREAM_BYTES, "merge area fits");
+    static_assert(LDS <= 160 * 1024, "fits the LDS of one CU");
+    static_assert(4 * ROWS <= THREADS, "four finishing threads per row");
+    static_assert(SLOTS <= 16 && 1024 % D == 0, "the key swizzle repeats every 1 KB");
 };
 
 // ---- direct-to-LDS DMA through inline asm: the compiler does not track these loads, so
@@ -103,7 +117,7 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
-// wait until at most n later chunks (of LOADS instructions each) are still in flight
+// wait until at most n (0..2) later chunks of LOADS instructions each are still in flight
 template <int LOADS>
 __device__ __forceinline__ void wait_chunks_after(int n) {
     if (n >= 2) wait_vm<2 * LOADS>();
@@ -128,6 +142,24 @@ __device__ __forceinline__ h8 codes_to_h8(uint2 raw) {
     return __builtin_bit_cast(h8, u);
 }
 
+// maximum and sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (cross-lane swaps, no LDS)
+__device__ __forceinline__ float max_over_j(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_j(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float centroid_full(uint32_t code, const CodebookHalf& cb) {
     const uint32_t m = code >= 4u ? code - 4u : 3u - code;
     const float mag = (m & 2u) ? ((m & 1u) ? cb.centroid_pos[3] : cb.centroid_pos[2])
@@ -143,63 +175,87 @@ struct TileSrc {
     int T;
 };
 
-// Score wave: DMA of the keys, block scales and norms of chunk c. Key rows keep their
+// Keys, block scales and norms of chunk c into one key stage. Key rows keep their
 // 16-byte slots XOR-swizzled by the row index, so the 16 rows one fragment read touches
-// fall into distinct LDS banks. Rows past the end of the tile are clamped to the last
-// token (valid memory; those tokens are masked out of the softmax).
-template <int D, int NRB>
-__device__ __forceinline__ void issue_keys(const TileSrc& ts, const uint32_t (&krow)[MCfg<D, NRB>::K_INSTR],
-                                           const uint32_t (&kseg)[MCfg<D, NRB>::K_INSTR], int c,
-                                           uint8_t* stage, int lane) {
-    using C = MCfg<D, NRB>;
-    const int t0 = c * CHUNK;
-    const int T = ts.T;
-    const bool full = t0 + CHUNK <= T;
-    const int8_t* kb = ts.kcodes + (size_t)t0 * D;
-#pragma unroll
-    for (int i = 0; i < C::K_INSTR; ++i) {
-        uint32_t row = krow[i];
-        if (!full) row = min(row, (uint32_t)(T - 1 - t0));
-        dma16(kb, row * D + kseg[i], lds_addr(stage + C::A_OFF_K + i * 1024));
-    }
+// fall into distinct LDS banks; one DMA instruction moves 1 KB, and the swizzle repeats
+// every 1 KB, so instruction i reads koff + 1 KB * i. In the tile's last, partial chunk,
+// rows past the end of the tile are clamped to the last token (valid memory; those
+// tokens get weight 0 in the softmax).
+__device__ __forceinline__ uint32_t lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// The lane offsets are derived from the lane id where they are used, so that nothing
+// stays live across the score loop for them.
+template <class C, bool FULL>
+__device__ __forceinline__ void issue_keys(const TileSrc& ts, int c, uint8_t* stage) {
+    constexpr int D = C::SLOTS * 16;
     constexpr int per_tok = C::NB * 2;
-    if (lane < C::S_LANES) {
-        const int o = 4 * lane;
-        int row = o / per_tok;
-        if (!full) row = min(row, T - 1 - t0);
-        dma4(ts.kscales + (size_t)t0 * per_tok, (uint32_t)(row * per_tok + (o % per_tok)),
-             lds_addr(stage + C::A_OFF_S));
-    }
-    if (lane < 16) {
-        int row = 2 * lane;
-        if (!full && row > T - 1 - t0) row = (T - 1 - t0) & ~1;
-        dma4(ts.vnorms + (size_t)t0 * 2, (uint32_t)(row * 2), lds_addr(stage + C::A_OFF_N));
-    }
-}
-
-// Value wave: DMA of the three bit-planes of chunk c (always inside the tile).
-template <int D, int NRB>
-__device__ __forceinline__ void issue_values(const TileSrc& ts, int c, uint8_t* stage, int lane) {
-    using C = MCfg<D, NRB>;
-    const uint8_t* vg = ts.vplanes + (size_t)c * C::V_BYTES;
+    constexpr int ROWS_PER_INSTR = 1024 / D;
+    const uint32_t lane = lane_id();
+    const uint32_t krow = 16u * lane / D;
+    const uint32_t koff = krow * D + (((16u * lane) % D) / 16 ^ (krow & (C::SLOTS - 1))) * 16;
+    const uint32_t soff = 4u * lane, noff = 4u * lane;
+    const int t0 = c * CHUNK;
+    const int8_t* kb = ts.kcodes + (size_t)t0 * D;
+    const uint8_t* sb = ts.kscales + (size_t)t0 * per_tok;
+    const uint8_t* nb = ts.vnorms + (size_t)t0 * 2;
+    if constexpr (FULL) {
 #pragma unroll
-    for (int i = 0; i < C::V_INSTR; ++i) {
-        const bool tail = (i == C::V_INSTR - 1) && C::V_TAIL_LANES != 0;
-        if (!tail || lane < C::V_TAIL_LANES)
-            dma16(vg, (uint32_t)(i * 1024 + 16 * lane), lds_addr(stage + i * 1024));
+        for (int i = 0; i < C::K_INSTR; ++i) dma16(kb + 1024 * i, koff, lds_addr(stage + i * 1024));
+        if (lane < (uint32_t)C::S_LANES) dma4(sb, soff, lds_addr(stage + C::A_OFF_S));
+        if (lane < 16u) dma4(nb, noff, lds_addr(stage + C::A_OFF_N));
+    } else {
+        // from the chunk base: the clamped row plus the lane's swizzled slot (which is the
+        // same in every instruction); never a negative offset
+        const uint32_t last = (uint32_t)(ts.T - 1 - t0);
+        const uint32_t slot16 = koff - krow * D;
+#pragma unroll
+        for (int i = 0; i < C::K_INSTR; ++i) {
+            const uint32_t row = krow + ROWS_PER_INSTR * i;
+            dma16(kb, min(row, last) * D + slot16, lds_addr(stage + i * 1024));
+        }
+        if (lane < (uint32_t)C::S_LANES) {
+            const uint32_t row = soff / per_tok;
+            dma4(sb, soff - (row - min(row, last)) * per_tok, lds_addr(stage + C::A_OFF_S));
+        }
+        if (lane < 16u) {
+            const uint32_t row = noff / 2;
+            dma4(nb, row > last ? 2 * (last & ~1u) : noff, lds_addr(stage + C::A_OFF_N));
+        }
+    }
+}
+template <class C>
+__device__ __forceinline__ void issue_keys_any(const TileSrc& ts, int c, uint8_t* stage) {
+    if ((c + 1) * CHUNK <= ts.T) issue_keys<C, true>(ts, c, stage);
+    else issue_keys<C, false>(ts, c, stage);
+}
+
+// Value wave `half`: its half of the three bit-planes of chunk c (always inside the tile),
+// as [plane][HD] words at the start of its half of the plane stage.
+template <class C>
+__device__ __forceinline__ void issue_planes(const TileSrc& ts, int c, int half, uint8_t* stage) {
+    constexpr int D = C::SLOTS * 16;
+    const int lane = (int)lane_id();
+    if (lane < C::V_LANES) {
+        const int p = lane / C::LPP, seg = lane - p * C::LPP;
+        const uint8_t* vg = ts.vplanes + (size_t)c * (3 * D * 4);
+        dma16(vg, (uint32_t)(p * D * 4 + half * C::HD * 4 + 16 * seg), lds_addr(stage + half * C::VH_BYTES));
     }
 }
 
-template <int D, int NRB>
-__global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
-    using C = MCfg<D, NRB>;
-    constexpr int NB = C::NB, NDB = C::NDB, ROWS = C::ROWS;
+template <int D, int SRB, int NSW>
+__global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(AttendArgs a) {
+    using C = MCfg<D, SRB, NSW>;
+    constexpr int NB = C::NB, NRB = C::NRB, ROWS = C::ROWS, VDB = C::VDB, HD = C::HD;
+    constexpr int AL_STRIDE = C::AL_STRIDE;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
-    const int pair = w & (PAIRS - 1);
-    const bool score_wave = w < PAIRS;
+    const int stream = w % STREAMS;
+    const int role = w / STREAMS;                            // < NSW: score wave
+    const bool score_wave = role < NSW;
     const int l16 = lane & 15;
     const int j = lane >> 4;
 
@@ -217,71 +273,27 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
     ts.T = T;
 
     const int NC = (T + CHUNK - 1) / CHUNK;
-    const int nk = pair < NC ? (NC - pair + PAIRS - 1) / PAIRS : 0;  // chunks of this pair
-    const int nk_max = (NC + PAIRS - 1) / PAIRS;                      // same for every wave
-    uint8_t* pbase = lds + C::OFF_PAIRS + pair * C::PAIR_BYTES;
-    uint8_t* aring = pbase + C::PAIR_OFF_A;
-    uint8_t* bring = pbase + C::PAIR_OFF_B;
-    h8* pbuf = reinterpret_cast<h8*>(pbase + C::PAIR_OFF_P);          // [2][NRB][64]
-    float* albuf = reinterpret_cast<float*>(pbase + C::PAIR_OFF_AL);  // [2][ROWS + 4]
-    constexpr int AL_STRIDE = ROWS + 4;
-
-    // per-lane DMA offsets of the key rows (independent of the chunk)
-    uint32_t krow[C::K_INSTR], kseg[C::K_INSTR];
-#pragma unroll
-    for (int i = 0; i < C::K_INSTR; ++i) {
-        const int o = i * 1024 + 16 * lane;
-        const int tt = o / D;
-        const int slot = (o % D) / 16;
-        krow[i] = (uint32_t)tt;
-        kseg[i] = (uint32_t)((slot ^ (tt & (C::SLOTS - 1))) * 16);
-    }
-    // start streaming: the score wave two chunks ahead, the value wave likewise
-    if (score_wave) {
-        for (int s = 0; s < NSTAGE - 1; ++s)
-            if (s < nk) issue_keys<D, NRB>(ts, krow, kseg, pair + PAIRS * s, aring + s * C::A_STAGE, lane);
-    } else {
-        for (int s = 0; s < NSTAGE - 1; ++s)
-            if (s < nk) issue_values<D, NRB>(ts, pair + PAIRS * s, bring + s * C::B_STAGE, lane);
-    }
-
-    // value lookup table: entry e -> lambda * the centroids of the 4 tokens whose plane bits
-    // are the nibbles (e & 15, (e >> 4) & 15, e >> 8), in fp16
-    {
-        h4* lut = reinterpret_cast<h4*>(lds + C::OFF_LUT);
-        const float lam = a.cb.fp16_scale;
-        for (int e = tid; e < 4096; e += 512) {
-            h4 v;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t code = ((e >> u) & 1) | (((e >> (4 + u)) & 1) << 1) | (((e >> (8 + u)) & 1) << 2);
-                v[u] = (_Float16)(lam * centroid_full(code, a.cb));
-            }
-            lut[e] = v;
-        }
-    }
-    __syncthreads();
-
+    const int nk = stream < NC ? (NC - stream + STREAMS - 1) / STREAMS : 0;  // this stream
+    const int nk_max = (NC + STREAMS - 1) / STREAMS;                         // every stream
+    uint8_t* sbase = lds + C::OFF_STREAMS + stream * C::STREAM_BYTES;
+    uint8_t* aring = sbase + C::ST_OFF_A;
+    uint8_t* bring = sbase + C::ST_OFF_B;
+    h8* pbuf = reinterpret_cast<h8*>(sbase + C::ST_OFF_P);          // [2][NRB][64]
+    float* albuf = reinterpret_cast<float*>(sbase + C::ST_OFF_AL);  // [2][AL_STRIDE]
     const size_t HG = (size_t)H * G;
-    float m_ref[NRB], l_run[NRB];  // score wave: per row l16 of each row block
-    f4 O[NRB][NDB];                // value wave: rows 16rb + 4j + i, dim 16db + l16
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        m_ref[rb] = -INFINITY;
-        l_run[rb] = 0.0f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) O[rb][db] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
 
+    // ---- score waves: queries (B operand). Lane holds row 16 rb + l16 of its row
+    // blocks, dims 32b + 8j .. +7, times scale * log2(e), as fp16 hi + lo. Loaded before
+    // any DMA is issued so that the compiler's own vmcnt waits do not wait on the DMA.
+    h8 qh[SRB][NB], ql[SRB][NB];
+    float m_ref[SRB], l_run[SRB];
     if (score_wave) {
-        // ===================== score wave =====================
-        // query rows (B operand): lane holds row 16rb + l16, dims 32b + 8j .. +7, times
-        // scale * log2(e), as fp16 hi + lo
         const float qs = a.softmax_scale * kLog2e;
-        h8 qh[NRB][NB], ql[NRB][NB];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            const int r = 16 * rb + l16;
+        for (int rb = 0; rb < SRB; ++rb) {
+            m_ref[rb] = -INFINITY;
+            l_run[rb] = 0.0f;
+            const int r = 16 * (SRB * role + rb) + l16;
             const float* qrow = nullptr;
             if (r < R) {
                 const int ag = r / G, jj = r - ag * G;
@@ -308,48 +320,95 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
                 }
             }
         }
-        // LDS offsets (within a stage) of the key fragments: token 16tb + l16, dims
-        // 32b + 8j .. +7, through the row swizzle
-        uint32_t kfrag[2][NB];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int tt = 16 * tb + l16;
-                const int seg = 2 * b + (j >> 1);
-                const int slot = seg ^ (tt & (C::SLOTS - 1));
-                kfrag[tb][b] = (uint32_t)(C::A_OFF_K + tt * D + slot * 16 + 8 * (j & 1));
-            }
+    }
 
-        for (int k = 0; k < nk_max; ++k) {
+    // value lookup table: entry e -> lambda * the centroids of the 4 tokens whose plane bits
+    // are the nibbles (e & 15, (e >> 4) & 15, e >> 8), in fp16
+    {
+        h4* lut = reinterpret_cast<h4*>(lds + C::OFF_LUT);
+        const float lam = a.cb.fp16_scale;
+        for (int e = tid; e < 4096; e += C::THREADS) {
+            h4 v;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t code = ((e >> u) & 1) | (((e >> (4 + u)) & 1) << 1) | (((e >> (8 + u)) & 1) << 2);
+                v[u] = (_Float16)(lam * centroid_full(code, a.cb));
+            }
+            lut[e] = v;
+        }
+    }
+
+    // token weights of a full chunk (all 1) and of the tile's last chunk (1 below T)
+    if (tid < 2 * CHUNK) {
+        const int t = tid & (CHUNK - 1);
+        const bool tail = tid >= CHUNK;
+        reinterpret_cast<_Float16*>(lds + C::OFF_MASK)[tid] =
+            (!tail || (NC - 1) * CHUNK + t < T) ? (_Float16)1.0f : (_Float16)0.0f;
+    }
+    // start streaming NSTAGE - 1 chunks ahead; the first key chunk must have landed before
+    // the first barrier publishes it
+    const bool key_wave = score_wave && role == 0;
+    if (key_wave) {
+        for (int s = 0; s < NSTAGE - 1; ++s)
+            if (s < nk) issue_keys_any<C>(ts, stream + STREAMS * s, aring + s * C::A_STAGE);
+        wait_chunks_after<C::A_LOADS>(min(NSTAGE - 2, nk - 1));
+    } else if (!score_wave) {
+        for (int s = 0; s < NSTAGE - 1; ++s)
+            if (s < nk) issue_planes<C>(ts, stream + STREAMS * s, role - NSW, bring + s * C::B_STAGE);
+    }
+    __syncthreads();
+
+    f4 O[NRB][VDB];  // value waves: rows 16 rb + 4j + i, dims HD * half + VDB * l16 + db
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int db = 0; db < VDB; ++db) O[rb][db] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (score_wave) {
+        // ===================== score waves =====================
+        // LDS offsets (within a stage) of the key fragments: token l16, dims 32b + 8j .. +7,
+        // through the row swizzle
+        // (token block tb adds 16 * D: the swizzle depends only on the low row bits)
+        uint32_t kfrag[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int seg = 2 * b + (j >> 1);
+            const int slot = seg ^ (l16 & (C::SLOTS - 1));
+            kfrag[b] = (uint32_t)(l16 * D + slot * 16 + 8 * (j & 1));
+        }
+
+        for (int k = 0; k <= nk_max; ++k) {
             if (k < nk) {
-                const int c = pair + PAIRS * k;
+                const int c = stream + STREAMS * k;
                 const int t0 = c * CHUNK;
-                if (k + NSTAGE - 1 < nk)
-                    issue_keys<D, NRB>(ts, krow, kseg, c + PAIRS * (NSTAGE - 1),
-                                       aring + ((k + NSTAGE - 1) % NSTAGE) * C::A_STAGE, lane);
-                wait_chunks_after<C::A_LOADS>(min(NSTAGE - 1, nk - 1 - k));
+                if (key_wave && k + NSTAGE - 1 < nk)
+                    issue_keys_any<C>(ts, c + STREAMS * (NSTAGE - 1),
+                                      aring + ((k + NSTAGE - 1) % NSTAGE) * C::A_STAGE);
                 const uint8_t* st = aring + (k % NSTAGE) * C::A_STAGE;
                 const h4 n_lo = *reinterpret_cast<const h4*>(st + C::A_OFF_N + 8 * j);
                 const h4 n_hi = *reinterpret_cast<const h4*>(st + C::A_OFF_N + 32 + 8 * j);
+                // token weights: 1, or 0 for the tokens past T in the tile's last chunk
+                const uint8_t* wm = lds + C::OFF_MASK + (t0 + CHUNK > T ? 64 : 0);
+                const h4 m_lo = *reinterpret_cast<const h4*>(wm + 8 * j);
+                const h4 m_hi = *reinterpret_cast<const h4*>(wm + 32 + 8 * j);
                 const bool first = k == 0;
-                f4 S[2][NRB];
+                f4 S[2][SRB];
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
-                    h8 scv[NB / 2];
+                    h8 scv[(NB + 1) / 2];
                     const h8* sp = reinterpret_cast<const h8*>(st + C::A_OFF_S + (16 * tb + 4 * j) * NB * 2);
 #pragma unroll
-                    for (int v = 0; v < NB / 2; ++v) scv[v] = sp[v];
+                    for (int v = 0; v < (NB + 1) / 2; ++v) scv[v] = sp[v];
 #pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) {
+                    for (int rb = 0; rb < SRB; ++rb) {
                         const float init = first ? 0.0f : -(m_ref[rb] + kSlack);
                         S[tb][rb] = f4{init, init, init, init};
                     }
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
-                        const h8 ak = codes_to_h8(*reinterpret_cast<const uint2*>(st + kfrag[tb][b]));
+                        const h8 ak = codes_to_h8(*reinterpret_cast<const uint2*>(st + 16 * D * tb + kfrag[b]));
 #pragma unroll
-                        for (int rb = 0; rb < NRB; ++rb) {
+                        for (int rb = 0; rb < SRB; ++rb) {
                             f4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qh[rb][b], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
                             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, ql[rb][b], acc, 0, 0, 0);
 #pragma unroll
@@ -360,20 +419,12 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
                         }
                     }
                 }
-                if (t0 + CHUNK > T) {
-#pragma unroll
-                    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (t0 + 16 * tb + 4 * j + i >= T)
-#pragma unroll
-                                for (int rb = 0; rb < NRB; ++rb) S[tb][rb][i] = -INFINITY;
-                }
                 // reference maxima: exact on the first chunk; afterwards raised only when a
-                // score exceeds m_ref + slack (then the value wave rescales its rows)
+                // score exceeds m_ref + slack (then the value waves rescale these rows).
+                // Tokens past T carry the last token's score, so they never raise it.
                 float mx = -INFINITY;
 #pragma unroll
-                for (int rb = 0; rb < NRB; ++rb)
+                for (int rb = 0; rb < SRB; ++rb)
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -382,14 +433,13 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
                 const bool raise = __any(first || mx > 0.0f);
                 if (raise) {
 #pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) {
+                    for (int rb = 0; rb < SRB; ++rb) {
                         float cm = -INFINITY;
 #pragma unroll
                         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) cm = fmaxf(cm, S[tb][rb][i]);
-                        cm = fmaxf(cm, __shfl_xor(cm, 16));
-                        cm = fmaxf(cm, __shfl_xor(cm, 32));
+                        cm = max_over_j(cm);
                         float shift, alpha;
                         if (first) {
                             m_ref[rb] = cm;
@@ -401,64 +451,84 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
                             alpha = __builtin_amdgcn_exp2f(-shift);
                             l_run[rb] *= alpha;
                         }
-                        if (j == 0) al[16 * rb + l16] = alpha;
+                        if (j == 0) al[16 * (SRB * role + rb) + l16] = alpha;
 #pragma unroll
                         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) S[tb][rb][i] -= shift;
                     }
                 }
-                if (lane == 0) al[ROWS] = (raise && !first) ? 1.0f : 0.0f;
-                // probabilities (scaled by 2^-slack), row sums, P.V operand p * n
-                const h8 nn = {n_lo[0], n_lo[1], n_lo[2], n_lo[3], n_hi[0], n_hi[1], n_hi[2], n_hi[3]};
+                if (lane == 0) al[ROWS + role] = (raise && !first) ? 1.0f : 0.0f;
+                // probabilities (scaled by 2^-slack) in fp16; row sums of the weighted fp16
+                // probabilities; P.V operand p * n * weight
+                const h8 wt = {m_lo[0], m_lo[1], m_lo[2], m_lo[3], m_hi[0], m_hi[1], m_hi[2], m_hi[3]};
+                const h8 nn = h8{n_lo[0], n_lo[1], n_lo[2], n_lo[3], n_hi[0], n_hi[1], n_hi[2], n_hi[3]} * wt;
                 h8* pb = pbuf + (k & 1) * NRB * 64;
 #pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    float p[8];
+                for (int rb = 0; rb < SRB; ++rb) {
+                    h8 ph;
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) p[4 * tb + i] = __builtin_amdgcn_exp2f(S[tb][rb][i]);
-                    l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-                    const h8 ph = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
-                                   (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
-                    pb[rb * 64 + lane] = ph * nn;
+                        for (int i = 0; i < 4; ++i) ph[4 * tb + i] = (_Float16)__builtin_amdgcn_exp2f(S[tb][rb][i]);
+                    float l = l_run[rb];
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2)
+                        l = __builtin_amdgcn_fdot2(h2{ph[e], ph[e + 1]}, h2{wt[e], wt[e + 1]}, l, false);
+                    l_run[rb] = l;
+                    pb[(SRB * role + rb) * 64 + lane] = ph * nn;
                 }
+                // the next key chunk must have landed before the barrier publishes it
+                if (key_wave) wait_chunks_after<C::A_LOADS>(max(0, min(NSTAGE - 2, nk - 2 - k)));
             }
-            __syncthreads();  // probabilities of chunk k are visible to the value wave
+            __syncthreads();
         }
-        __syncthreads();      // matches the value wave's extra (last) step
     } else {
-        // ===================== value wave =====================
+        // ===================== value waves =====================
+        const int half = role - NSW;
         const h4* lut = reinterpret_cast<const h4*>(lds + C::OFF_LUT);
         const uint32_t sh = 4u * (uint32_t)j;
-        __syncthreads();  // step -1: nothing to consume yet
-        for (int k = 0; k < nk_max; ++k) {
-            if (k < nk) {
-                if (k + NSTAGE - 1 < nk)
-                    issue_values<D, NRB>(ts, pair + PAIRS * (k + NSTAGE - 1),
-                                         bring + ((k + NSTAGE - 1) % NSTAGE) * C::B_STAGE, lane);
-                wait_chunks_after<C::B_LOADS>(min(NSTAGE - 1, nk - 1 - k));
-                const float* al = albuf + (k & 1) * AL_STRIDE;
-                if (al[ROWS] != 0.0f) {
+        for (int k = 0; k <= nk_max; ++k) {
+            const int kk = k - 1;  // one chunk behind the score waves
+            if (kk >= 0 && kk < nk) {
+                if (kk + NSTAGE - 1 < nk)
+                    issue_planes<C>(ts, stream + STREAMS * (kk + NSTAGE - 1), half,
+                                    bring + ((kk + NSTAGE - 1) % NSTAGE) * C::B_STAGE);
+                wait_chunks_after<1>(min(NSTAGE - 1, nk - 1 - kk));
+                const float* al = albuf + (kk & 1) * AL_STRIDE;
 #pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb)
+                for (int r = 0; r < NSW; ++r) {
+                    if (al[ROWS + r] != 0.0f) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float ai = al[16 * rb + 4 * j + i];
+                        for (int rb = SRB * r; rb < SRB * (r + 1); ++rb)
 #pragma unroll
-                            for (int db = 0; db < NDB; ++db) O[rb][db][i] *= ai;
-                        }
+                            for (int i = 0; i < 4; ++i) {
+                                const float ai = al[16 * rb + 4 * j + i];
+#pragma unroll
+                                for (int db = 0; db < VDB; ++db) O[rb][db][i] *= ai;
+                            }
+                    }
                 }
-                const h8* pb = pbuf + (k & 1) * NRB * 64;
+                const h8* pb = pbuf + (kk & 1) * NRB * 64;
                 h8 ap[NRB];
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb) ap[rb] = pb[rb * 64 + lane];
-                const uint32_t* vw = reinterpret_cast<const uint32_t*>(bring + (k % NSTAGE) * C::B_STAGE);
+                // plane words of this lane's VDB consecutive dimensions
+                const uint8_t* vs = bring + (kk % NSTAGE) * C::B_STAGE + half * C::VH_BYTES + 4 * VDB * l16;
+                uint32_t wv[3][VDB];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int dim = 16 * db + l16;
-                    const uint32_t w0 = vw[dim], w1 = vw[D + dim], w2 = vw[2 * D + dim];
+                for (int p = 0; p < 3; ++p) {
+                    if constexpr (VDB == 4) {
+                        const uint4 u = *reinterpret_cast<const uint4*>(vs + p * HD * 4);
+                        wv[p][0] = u.x; wv[p][1] = u.y; wv[p][2] = u.z; wv[p][3] = u.w;
+                    } else {
+                        const uint2 u = *reinterpret_cast<const uint2*>(vs + p * HD * 4);
+                        wv[p][0] = u.x; wv[p][1] = u.y;
+                    }
+                }
+#pragma unroll
+                for (int db = 0; db < VDB; ++db) {
+                    const uint32_t w0 = wv[0][db], w1 = wv[1][db], w2 = wv[2][db];
                     const uint32_t ilo = __builtin_amdgcn_ubfe(w0, sh, 4) | (__builtin_amdgcn_ubfe(w1, sh, 4) << 4) |
                                          (__builtin_amdgcn_ubfe(w2, sh, 4) << 8);
                     const uint32_t ihi = __builtin_amdgcn_ubfe(w0, sh + 16u, 4) |
@@ -471,29 +541,29 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
                         O[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[rb], bv, O[rb][db], 0, 0, 0);
                 }
             }
-            __syncthreads();  // done with the probabilities of chunk k
+            __syncthreads();
         }
     }
 
-    // ---- merge the pairs and finish the rows ----
-    float* mw = reinterpret_cast<float*>(lds + C::OFF_PAIRS);  // [PAIRS][ROWS]
-    float* lw = mw + PAIRS * ROWS;                              // [PAIRS][ROWS]
-    float* ob = lw + PAIRS * ROWS;                              // [2][ROWS][D]
+    // ---- merge the streams and finish the rows ----
+    float* mw = reinterpret_cast<float*>(lds + C::OFF_STREAMS);  // [STREAMS][ROWS]
+    float* lw = mw + STREAMS * ROWS;                              // [STREAMS][ROWS]
+    float* ob = lw + STREAMS * ROWS;                              // [2][ROWS][D]
     if (score_wave) {
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            float l = l_run[rb];
-            l += __shfl_xor(l, 16);
-            l += __shfl_xor(l, 32);
+        for (int rb = 0; rb < SRB; ++rb) {
+            const float l = sum_over_j(l_run[rb]);
             if (j == 0) {
-                mw[pair * ROWS + 16 * rb + l16] = m_ref[rb];
-                lw[pair * ROWS + 16 * rb + l16] = l;
+                const int row = 16 * (SRB * role + rb) + l16;
+                mw[stream * ROWS + row] = m_ref[rb];
+                lw[stream * ROWS + row] = l;
             }
         }
     }
     __syncthreads();
-    // the value wave of pair p weights its rows by 2^(m_p - M)
+    // the value waves of stream s weight their rows by 2^(m_s - M)
     float fo[NRB][4];
+    const int dim0 = HD * (role - NSW) + VDB * l16;
     if (!score_wave) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
@@ -502,29 +572,31 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
                 const int row = 16 * rb + 4 * j + i;
                 float M = -INFINITY;
 #pragma unroll
-                for (int v = 0; v < PAIRS; ++v) M = fmaxf(M, mw[v * ROWS + row]);
-                const float mine = mw[pair * ROWS + row];
+                for (int v = 0; v < STREAMS; ++v) M = fmaxf(M, mw[v * ROWS + row]);
+                const float mine = mw[stream * ROWS + row];
                 fo[rb][i] = mine == -INFINITY ? 0.0f : exp2f(mine - M);
             }
-        if (pair < 2) {
-            float* mybuf = ob + pair * ROWS * D;
+        if (stream < 2) {
+            float* mybuf = ob + stream * ROWS * D;
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) mybuf[(16 * rb + 4 * j + i) * D + 16 * db + l16] = O[rb][db][i] * fo[rb][i];
+                    for (int db = 0; db < VDB; ++db)
+                        mybuf[(16 * rb + 4 * j + i) * D + dim0 + db] = O[rb][db][i] * fo[rb][i];
         }
     }
     __syncthreads();
-    if (!score_wave && pair >= 2) {
-        float* mybuf = ob + (pair - 2) * ROWS * D;
+    if (!score_wave && stream >= 2) {
+        float* mybuf = ob + (stream - 2) * ROWS * D;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mybuf[(16 * rb + 4 * j + i) * D + 16 * db + l16] += O[rb][db][i] * fo[rb][i];
+                for (int db = 0; db < VDB; ++db)
+                    mybuf[(16 * rb + 4 * j + i) * D + dim0 + db] += O[rb][db][i] * fo[rb][i];
     }
     __syncthreads();
 
@@ -556,10 +628,10 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
         }
         float M = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < PAIRS; ++v) M = fmaxf(M, mw[v * ROWS + row]);
+        for (int v = 0; v < STREAMS; ++v) M = fmaxf(M, mw[v * ROWS + row]);
         float L = 0.0f;
 #pragma unroll
-        for (int v = 0; v < PAIRS; ++v) {
+        for (int v = 0; v < STREAMS; ++v) {
             const float mv = mw[v * ROWS + row];
             if (mv != -INFINITY) L += lw[v * ROWS + row] * exp2f(mv - M);
         }
@@ -574,14 +646,14 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(AttendArgs a) {
     }
 }
 
-template <int D, int NRB>
+template <int D, int SRB, int NSW>
 hipError_t launch_t(const AttendArgs& a, hipStream_t s) {
-    using C = MCfg<D, NRB>;
-    auto kern = k_attend_mfma<D, NRB>;
+    using C = MCfg<D, SRB, NSW>;
+    auto kern = k_attend_mfma<D, SRB, NSW>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     const uint32_t tiles = (uint32_t)a.layer_count * (uint32_t)a.g.n_kv_heads;
-    hipLaunchKernelGGL(kern, dim3(tiles), dim3(512), C::LDS, s, a);
+    hipLaunchKernelGGL(kern, dim3(tiles), dim3(C::THREADS), C::LDS, s, a);
     return hipGetLastError();
 }
 
@@ -595,14 +667,14 @@ hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
     const int rows = a.n_agents * a.gqa;
     const int nrb = (rows + 15) / 16;
     if (a.g.head_dim == 128) {
-        if (nrb == 1) return launch_t<128, 1>(a, s);
-        if (nrb == 2) return launch_t<128, 2>(a, s);
-        return launch_t<128, 4>(a, s);
+        if (nrb == 1) return launch_t<128, 1, 1>(a, s);
+        if (nrb == 2) return launch_t<128, 1, 2>(a, s);
+        return launch_t<128, 2, 2>(a, s);
     }
     if (a.g.head_dim == 64) {
-        if (nrb == 1) return launch_t<64, 1>(a, s);
-        if (nrb == 2) return launch_t<64, 2>(a, s);
-        return launch_t<64, 4>(a, s);
+        if (nrb == 1) return launch_t<64, 1, 1>(a, s);
+        if (nrb == 2) return launch_t<64, 1, 2>(a, s);
+        return launch_t<64, 2, 2>(a, s);
     }
     return hipErrorInvalidValue;
 }
