@@ -21,8 +21,8 @@
 //   accumulates P.V for every row in fp32, one chunk behind the score waves. Four waves
 //   of similar register size per SIMD hide each other's latencies;
 // - the first score wave of a stream streams the keys, block scales and norms of its
-//   chunks into an LDS ring by direct-to-LDS DMA; each value wave streams its half of
-//   the planes. One workgroup barrier per chunk step publishes keys and probabilities;
+//   chunks into a four-deep LDS ring by direct-to-LDS DMA (256-byte aligned
+//   destinations); each value wave streams its half of the planes into a three-deep ring. One workgroup barrier per chunk step publishes keys and probabilities;
 // - a row's reference maximum is raised only when a score exceeds it by more than 8
 //   (log2 units); the score wave then passes per-row rescale factors to the value waves;
 // - at the end the streams' (m, l, acc) are merged through LDS and each row becomes
@@ -44,7 +44,8 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int STREAMS = 4;
 constexpr int CHUNK = 32;
-constexpr int NSTAGE = 3;
+constexpr int NSK = 4;  // key ring depth (chunks)
+constexpr int NSV = 3;  // plane ring depth (chunks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.0f;  // log2 units a score may exceed the reference maximum
 
@@ -61,25 +62,29 @@ struct MCfg {
     static constexpr int SLOTS = D / 16;               // 16-byte slots in a key row
     static constexpr int HD = D / 2;                   // dimensions per value wave
     static constexpr int VDB = HD / 16;                // 16-column blocks per value wave
-    // key stage: key codes (rows XOR-swizzled by 16-byte slot), block scales, value norms
+    // Every DMA destination below is 256-byte aligned.
+    // key stage: key codes, rows XOR-swizzled by 16-byte slot
     static constexpr int K_BYTES = CHUNK * D;
+    // meta stage: block scales at 0, value norms at 256
     static constexpr int S_BYTES = CHUNK * NB * 2;
     static constexpr int N_BYTES = CHUNK * 2;
-    static constexpr int A_OFF_S = K_BYTES;
-    static constexpr int A_OFF_N = A_OFF_S + S_BYTES;
-    static constexpr int A_STAGE = round_up(A_OFF_N + N_BYTES, 256);
-    // plane stage: [value wave][plane][HD] words
+    static constexpr int M_OFF_S = 0;
+    static constexpr int M_OFF_N = 256;
+    static constexpr int M_STAGE = 512;
+    // plane stage: [value wave][plane][HD] words, each value wave's half 256-B aligned
     static constexpr int VH_BYTES = 3 * HD * 4;
+    static constexpr int VH_SLOT = round_up(VH_BYTES, 256);
     static constexpr int V_LANES = VH_BYTES / 16;      // lanes of the one DMA instruction
     static constexpr int LPP = HD * 4 / 16;            // lanes per plane
-    static constexpr int B_STAGE = round_up(2 * VH_BYTES, 256);
+    static constexpr int B_STAGE = 2 * VH_SLOT;
     // probabilities p * n (fp16 A operand of P.V, one h8 per lane and row block) and the
     // per-row rescale factors, then one flag per score wave
     static constexpr int P_BYTES = NRB * 64 * 16;
     static constexpr int AL_STRIDE = ROWS + 4;
-    static constexpr int ST_OFF_A = 0;
-    static constexpr int ST_OFF_B = ST_OFF_A + NSTAGE * A_STAGE;
-    static constexpr int ST_OFF_P = ST_OFF_B + NSTAGE * B_STAGE;
+    static constexpr int ST_OFF_K = 0;
+    static constexpr int ST_OFF_M = ST_OFF_K + NSK * K_BYTES;
+    static constexpr int ST_OFF_B = ST_OFF_M + NSK * M_STAGE;
+    static constexpr int ST_OFF_P = ST_OFF_B + NSV * B_STAGE;
     static constexpr int ST_OFF_AL = ST_OFF_P + 2 * P_BYTES;
     static constexpr int STREAM_BYTES = round_up(ST_OFF_AL + 2 * AL_STRIDE * 4, 256);
     static constexpr int LUT_BYTES = 4096 * 8;
@@ -97,6 +102,9 @@ struct MCfg {
     static_assert(S_LANES <= 64 && V_LANES <= 64, "one DMA instruction each");
     static_assert(MERGE_BYTES <= STREAMS * STREAM_BYTES, "merge area fits");
     static_assert(LDS <= 160 * 1024, "fits the LDS of one CU");
+    static_assert(NSK <= 4 && NSV <= 4 && 3 * A_LOADS <= 63, "wait_chunks_after covers the rings");
+    static_assert(S_BYTES <= 256 && N_BYTES <= 256 && K_BYTES % 256 == 0 && OFF_STREAMS % 256 == 0,
+                  "256-byte aligned DMA destinations");
     static_assert(4 * ROWS <= THREADS, "four finishing threads per row");
     static_assert(SLOTS <= 16 && 1024 % D == 0, "the key swizzle repeats every 1 KB");
 };
@@ -117,10 +125,11 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
-// wait until at most n (0..2) later chunks of LOADS instructions each are still in flight
+// wait until at most n (0..3) later chunks of LOADS instructions each are still in flight
 template <int LOADS>
 __device__ __forceinline__ void wait_chunks_after(int n) {
-    if (n >= 2) wait_vm<2 * LOADS>();
+    if (n >= 3) wait_vm<3 * LOADS>();
+    else if (n == 2) wait_vm<2 * LOADS>();
     else if (n == 1) wait_vm<LOADS>();
     else wait_vm<0>();
 }
@@ -181,14 +190,18 @@ struct TileSrc {
 // every 1 KB, so instruction i reads koff + 1 KB * i. In the tile's last, partial chunk,
 // rows past the end of the tile are clamped to the last token (valid memory; those
 // tokens get weight 0 in the softmax).
+// lane id, recomputed at every use: volatile so that the compiler neither hoists it (and
+// the offsets derived from it) out of the loop nor keeps it live across the loop
 __device__ __forceinline__ uint32_t lane_id() {
-    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    uint32_t r;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+    return r;
 }
 
 // The lane offsets are derived from the lane id where they are used, so that nothing
 // stays live across the score loop for them.
 template <class C, bool FULL>
-__device__ __forceinline__ void issue_keys(const TileSrc& ts, int c, uint8_t* stage) {
+__device__ __forceinline__ void issue_keys(const TileSrc& ts, int c, uint8_t* stage, uint8_t* meta) {
     constexpr int D = C::SLOTS * 16;
     constexpr int per_tok = C::NB * 2;
     constexpr int ROWS_PER_INSTR = 1024 / D;
@@ -203,8 +216,8 @@ __device__ __forceinline__ void issue_keys(const TileSrc& ts, int c, uint8_t* st
     if constexpr (FULL) {
 #pragma unroll
         for (int i = 0; i < C::K_INSTR; ++i) dma16(kb + 1024 * i, koff, lds_addr(stage + i * 1024));
-        if (lane < (uint32_t)C::S_LANES) dma4(sb, soff, lds_addr(stage + C::A_OFF_S));
-        if (lane < 16u) dma4(nb, noff, lds_addr(stage + C::A_OFF_N));
+        if (lane < (uint32_t)C::S_LANES) dma4(sb, soff, lds_addr(meta + C::M_OFF_S));
+        if (lane < 16u) dma4(nb, noff, lds_addr(meta + C::M_OFF_N));
     } else {
         // from the chunk base: the clamped row plus the lane's swizzled slot (which is the
         // same in every instruction); never a negative offset
@@ -217,18 +230,18 @@ __device__ __forceinline__ void issue_keys(const TileSrc& ts, int c, uint8_t* st
         }
         if (lane < (uint32_t)C::S_LANES) {
             const uint32_t row = soff / per_tok;
-            dma4(sb, soff - (row - min(row, last)) * per_tok, lds_addr(stage + C::A_OFF_S));
+            dma4(sb, soff - (row - min(row, last)) * per_tok, lds_addr(meta + C::M_OFF_S));
         }
         if (lane < 16u) {
             const uint32_t row = noff / 2;
-            dma4(nb, row > last ? 2 * (last & ~1u) : noff, lds_addr(stage + C::A_OFF_N));
+            dma4(nb, row > last ? 2 * (last & ~1u) : noff, lds_addr(meta + C::M_OFF_N));
         }
     }
 }
 template <class C>
-__device__ __forceinline__ void issue_keys_any(const TileSrc& ts, int c, uint8_t* stage) {
-    if ((c + 1) * CHUNK <= ts.T) issue_keys<C, true>(ts, c, stage);
-    else issue_keys<C, false>(ts, c, stage);
+__device__ __forceinline__ void issue_keys_any(const TileSrc& ts, int c, uint8_t* stage, uint8_t* meta) {
+    if ((c + 1) * CHUNK <= ts.T) issue_keys<C, true>(ts, c, stage, meta);
+    else issue_keys<C, false>(ts, c, stage, meta);
 }
 
 // Value wave `half`: its half of the three bit-planes of chunk c (always inside the tile),
@@ -240,7 +253,7 @@ __device__ __forceinline__ void issue_planes(const TileSrc& ts, int c, int half,
     if (lane < C::V_LANES) {
         const int p = lane / C::LPP, seg = lane - p * C::LPP;
         const uint8_t* vg = ts.vplanes + (size_t)c * (3 * D * 4);
-        dma16(vg, (uint32_t)(p * D * 4 + half * C::HD * 4 + 16 * seg), lds_addr(stage + half * C::VH_BYTES));
+        dma16(vg, (uint32_t)(p * D * 4 + half * C::HD * 4 + 16 * seg), lds_addr(stage + half * C::VH_SLOT));
     }
 }
 
@@ -276,7 +289,8 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
     const int nk = stream < NC ? (NC - stream + STREAMS - 1) / STREAMS : 0;  // this stream
     const int nk_max = (NC + STREAMS - 1) / STREAMS;                         // every stream
     uint8_t* sbase = lds + C::OFF_STREAMS + stream * C::STREAM_BYTES;
-    uint8_t* aring = sbase + C::ST_OFF_A;
+    uint8_t* kring = sbase + C::ST_OFF_K;
+    uint8_t* mring = sbase + C::ST_OFF_M;
     uint8_t* bring = sbase + C::ST_OFF_B;
     h8* pbuf = reinterpret_cast<h8*>(sbase + C::ST_OFF_P);          // [2][NRB][64]
     float* albuf = reinterpret_cast<float*>(sbase + C::ST_OFF_AL);  // [2][AL_STRIDE]
@@ -345,15 +359,15 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
         reinterpret_cast<_Float16*>(lds + C::OFF_MASK)[tid] =
             (!tail || (NC - 1) * CHUNK + t < T) ? (_Float16)1.0f : (_Float16)0.0f;
     }
-    // start streaming NSTAGE - 1 chunks ahead; the first key chunk must have landed before
-    // the first barrier publishes it
+    // start streaming NSK - 1 key chunks and NSV - 1 plane chunks ahead; the first key
+    // chunk must have landed before the first barrier publishes it
     const bool key_wave = score_wave && role == 0;
     if (key_wave) {
-        for (int s = 0; s < NSTAGE - 1; ++s)
-            if (s < nk) issue_keys_any<C>(ts, stream + STREAMS * s, aring + s * C::A_STAGE);
-        wait_chunks_after<C::A_LOADS>(min(NSTAGE - 2, nk - 1));
+        for (int s = 0; s < NSK - 1; ++s)
+            if (s < nk) issue_keys_any<C>(ts, stream + STREAMS * s, kring + s * C::K_BYTES, mring + s * C::M_STAGE);
+        wait_chunks_after<C::A_LOADS>(min(NSK - 2, nk - 1));
     } else if (!score_wave) {
-        for (int s = 0; s < NSTAGE - 1; ++s)
+        for (int s = 0; s < NSV - 1; ++s)
             if (s < nk) issue_planes<C>(ts, stream + STREAMS * s, role - NSW, bring + s * C::B_STAGE);
     }
     __syncthreads();
@@ -381,14 +395,21 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
             if (k < nk) {
                 const int c = stream + STREAMS * k;
                 const int t0 = c * CHUNK;
-                if (key_wave && k + NSTAGE - 1 < nk)
-                    issue_keys_any<C>(ts, c + STREAMS * (NSTAGE - 1),
-                                      aring + ((k + NSTAGE - 1) % NSTAGE) * C::A_STAGE);
-                const uint8_t* st = aring + (k % NSTAGE) * C::A_STAGE;
-                const h4 n_lo = *reinterpret_cast<const h4*>(st + C::A_OFF_N + 8 * j);
-                const h4 n_hi = *reinterpret_cast<const h4*>(st + C::A_OFF_N + 32 + 8 * j);
+                if (key_wave && k + NSK - 1 < nk)
+                    issue_keys_any<C>(ts, c + STREAMS * (NSK - 1), kring + ((k + NSK - 1) % NSK) * C::K_BYTES,
+                                      mring + ((k + NSK - 1) % NSK) * C::M_STAGE);
+                // stage offset in LDS: wave-uniform, so every lane address below is one
+                // scalar + vector add
+                const uint32_t st_off = (uint32_t)__builtin_amdgcn_readfirstlane(
+                    (int)(C::OFF_STREAMS + stream * C::STREAM_BYTES + C::ST_OFF_K + (k % NSK) * C::K_BYTES));
+                const uint32_t mt_off = (uint32_t)__builtin_amdgcn_readfirstlane(
+                    (int)(C::OFF_STREAMS + stream * C::STREAM_BYTES + C::ST_OFF_M + (k % NSK) * C::M_STAGE));
+                const uint8_t* st = lds + st_off;
+                const uint8_t* mt = lds + mt_off;
+                const h4 n_lo = *reinterpret_cast<const h4*>(mt + C::M_OFF_N + 8 * j);
+                const h4 n_hi = *reinterpret_cast<const h4*>(mt + C::M_OFF_N + 32 + 8 * j);
                 // token weights: 1, or 0 for the tokens past T in the tile's last chunk
-                const uint8_t* wm = lds + C::OFF_MASK + (t0 + CHUNK > T ? 64 : 0);
+                const uint8_t* wm = lds + (uint32_t)__builtin_amdgcn_readfirstlane(C::OFF_MASK + (t0 + CHUNK > T ? 64 : 0));
                 const h4 m_lo = *reinterpret_cast<const h4*>(wm + 8 * j);
                 const h4 m_hi = *reinterpret_cast<const h4*>(wm + 32 + 8 * j);
                 const bool first = k == 0;
@@ -396,7 +417,7 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
                     h8 scv[(NB + 1) / 2];
-                    const h8* sp = reinterpret_cast<const h8*>(st + C::A_OFF_S + (16 * tb + 4 * j) * NB * 2);
+                    const h8* sp = reinterpret_cast<const h8*>(mt + C::M_OFF_S + (16 * tb + 4 * j) * NB * 2);
 #pragma unroll
                     for (int v = 0; v < (NB + 1) / 2; ++v) scv[v] = sp[v];
 #pragma unroll
@@ -432,6 +453,7 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
                 float* al = albuf + (k & 1) * AL_STRIDE;
                 const bool raise = __any(first || mx > 0.0f);
                 if (raise) {
+                    asm volatile("" ::: "memory");  // rare: keep it out of the common path
 #pragma unroll
                     for (int rb = 0; rb < SRB; ++rb) {
                         float cm = -INFINITY;
@@ -479,7 +501,7 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
                     pb[(SRB * role + rb) * 64 + lane] = ph * nn;
                 }
                 // the next key chunk must have landed before the barrier publishes it
-                if (key_wave) wait_chunks_after<C::A_LOADS>(max(0, min(NSTAGE - 2, nk - 2 - k)));
+                if (key_wave) wait_chunks_after<C::A_LOADS>(max(0, min(NSK - 2, nk - 2 - k)));
             }
             __syncthreads();
         }
@@ -491,10 +513,10 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
         for (int k = 0; k <= nk_max; ++k) {
             const int kk = k - 1;  // one chunk behind the score waves
             if (kk >= 0 && kk < nk) {
-                if (kk + NSTAGE - 1 < nk)
-                    issue_planes<C>(ts, stream + STREAMS * (kk + NSTAGE - 1), half,
-                                    bring + ((kk + NSTAGE - 1) % NSTAGE) * C::B_STAGE);
-                wait_chunks_after<1>(min(NSTAGE - 1, nk - 1 - kk));
+                if (kk + NSV - 1 < nk)
+                    issue_planes<C>(ts, stream + STREAMS * (kk + NSV - 1), half,
+                                    bring + ((kk + NSV - 1) % NSV) * C::B_STAGE);
+                wait_chunks_after<1>(min(NSV - 1, nk - 1 - kk));
                 const float* al = albuf + (kk & 1) * AL_STRIDE;
 #pragma unroll
                 for (int r = 0; r < NSW; ++r) {
@@ -514,7 +536,9 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb) ap[rb] = pb[rb * 64 + lane];
                 // plane words of this lane's VDB consecutive dimensions
-                const uint8_t* vs = bring + (kk % NSTAGE) * C::B_STAGE + half * C::VH_BYTES + 4 * VDB * l16;
+                const uint32_t vs_off = (uint32_t)__builtin_amdgcn_readfirstlane(
+                    (int)(C::OFF_STREAMS + stream * C::STREAM_BYTES + C::ST_OFF_B + (kk % NSV) * C::B_STAGE + half * C::VH_SLOT));
+                const uint8_t* vs = lds + vs_off + 4 * VDB * l16;
                 uint32_t wv[3][VDB];
 #pragma unroll
                 for (int p = 0; p < 3; ++p) {
