@@ -24,6 +24,11 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-Wno-unused-command-line-argument"]
 
 
+# per-file extras: the value compressor keeps matrix-core results in ordinary vector
+# registers (its compares read them directly)
+FILE_FLAGS = {"compress.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc():
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -51,7 +56,8 @@ def build(verbose: bool = False) -> str:
     def compile_one(src):
         obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        _run([hipcc] + DEVICE_FLAGS + inc + lang + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([hipcc] + DEVICE_FLAGS + FILE_FLAGS.get(src, []) + inc + lang +
+             ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj
 
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:

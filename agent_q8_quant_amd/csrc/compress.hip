@@ -180,6 +180,142 @@ __global__ __launch_bounds__(256) void k_compress_v(const __half* __restrict__ v
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Values on the matrix cores (head_dim 64 and 128). One wave encodes one group of 32
+// tokens of one tile. The rotation y = H v runs as v_mfma_f32_32x32x16_f16 with the ±1
+// Sylvester matrix as the A operand (exact in fp16) and the fp16 values as the B operand
+// (exact; accumulation in fp32), so lane l ends up holding token l % 32 of the group at
+// output dims 32 mb + 8 (i / 4) + 4 (l / 32) + i % 4 (register i of block mb). A ballot
+// of one register over the wave is then two whole plane words: the low 32 bits belong to
+// one dim, the high 32 bits to the dim 4 further. Codes come from four compares per
+// register (sign and |y| against the three positive thresholds b * n), plane bits from
+// scalar logic on the ballots, and each word moves to the lane that stores it.
+// H[m][k] = (-1)^popcount(m & k); for the A fragment of output block mb and k step kk,
+// lane l holds m = 32 mb + l % 32, k = 16 kk + 8 (l / 32) + e, and the sign factors into
+// (-1)^(popcount(a & b) + (a >> 4) * (kk & 1)) * (-1)^popcount(mb & (kk >> 1)) with
+// a = l % 32 and b = 8 (l / 32) + e.
+// ---------------------------------------------------------------------------------------
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// lane `lane` (a constant once the loops are unrolled) of w := the wave-uniform value x
+__device__ __forceinline__ void put_lane(uint32_t& w, uint32_t x, int lane) {
+    asm("v_writelane_b32 %0, %1, %2" : "+v"(w) : "s"(x), "i"(lane));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_compress_v_mfma(const __half* __restrict__ v,
+                                                         uint8_t* __restrict__ pool, PoolGeom g,
+                                                         CodebookHalf cb, int32_t layer_begin,
+                                                         uint32_t n_items) {
+    constexpr int KK = D / 16;        // k steps of the rotation
+    constexpr int MB = D / 32;        // 32-dim output blocks
+    constexpr int WPL = 3 * D / 64;   // plane words per lane of the store
+    const int lane = threadIdx.x & 63;
+    const int l32 = lane & 31, hl = lane >> 5;
+    // wave-uniform (and known to be so: scalar registers and branches)
+    const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256u + threadIdx.x) >> 6));
+    if (item >= n_items) return;  // whole waves only
+    const uint32_t G = (uint32_t)g.n_groups;
+    const uint32_t T = (uint32_t)g.n_tokens;
+    const uint32_t tile_local = item / G;
+    const uint32_t grp = item - tile_local * G;
+    const uint32_t token = grp * 32u + (uint32_t)l32;
+    const bool valid = token < T;
+
+    // Sylvester fragments for even and odd k steps
+    h8 F[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int b = 8 * hl + e;
+        const int base = __builtin_popcount(l32 & b) & 1;
+        F[0][e] = base ? (_Float16)-1.0f : (_Float16)1.0f;
+        F[1][e] = (base ^ (l32 >> 4)) ? (_Float16)-1.0f : (_Float16)1.0f;
+    }
+
+    // B operand: token l % 32, dims 16 kk + 8 (l / 32) .. +7 (16 contiguous bytes)
+    h8 vb[KK];
+    {
+        const h8* src = reinterpret_cast<const h8*>(v + ((size_t)tile_local * T + (valid ? token : 0u)) * D + 8 * hl);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) vb[kk] = valid ? src[2 * kk] : h8{};
+    }
+
+    // squared norm in fp32 (each lane holds half of the token's dims)
+    float ss = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const h2 x = {vb[kk][e], vb[kk][e + 1]};
+            ss = __builtin_amdgcn_fdot2(x, x, ss, false);
+        }
+    {
+        const uint32_t u = __float_as_uint(ss);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        ss = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const float n = sqrtf(ss);
+    // y / n > b  <=>  y > b n for n > 0; n = 0 gives y = 0 and infinite thresholds (every
+    // code 3). Tokens past T have y = 0 and get thresholds -1: then every plane bit below
+    // comes out 0, as the layout requires.
+    const float inv_t = valid ? (n > 0.0f ? 1.0f : INFINITY) : -1.0f;
+    const float t4 = n > 0.0f ? cb.boundary_pos[0] * n : inv_t;
+    const float t5 = n > 0.0f ? cb.boundary_pos[1] * n : inv_t;
+    const float t6 = n > 0.0f ? cb.boundary_pos[2] * n : inv_t;
+
+    uint32_t wv[WPL];
+#pragma unroll
+    for (int r = 0; r < WPL; ++r) wv[r] = 0u;
+
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        f16v y = {};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const bool neg = __builtin_popcount(mb & (kk >> 1)) & 1;
+            const h8 a = neg ? -F[kk & 1] : F[kk & 1];
+            y = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, vb[kk], y, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float yy = y[i];
+            const float ay = fabsf(yy);
+            const uint64_t pos = __ballot(yy > 0.0f);
+            const uint64_t c4 = __ballot(ay > t4);
+            const uint64_t c5 = __ballot(ay > t5);
+            const uint64_t c6 = __ballot(ay > t6);
+            // code = 4 + m for y > 0, 3 - m otherwise, m = c4 + c5 + c6 (thermometer):
+            // bit 2 = sign, bit 1 = c5 xnor sign, bit 0 = (c4 ^ c5 ^ c6) xnor sign.
+            // (For y < 0 exactly on a boundary this gives the higher code.)
+            uint64_t pl[3];
+            pl[2] = pos;
+            pl[1] = ~(c5 ^ pos);
+            pl[0] = ~(c4 ^ c5 ^ c6 ^ pos);
+            // word (p, d) of the group goes to lane (p D + d) % 64 of register (p D + d) / 64;
+            // the ballot covers dims d0 (low half) and d0 + 4 (high half)
+            const int d0 = 32 * mb + 8 * (i / 4) + (i % 4);
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                const int w0 = p * D + d0, w1 = w0 + 4;
+                put_lane(wv[w0 / 64], (uint32_t)pl[p], w0 % 64);
+                put_lane(wv[w1 / 64], (uint32_t)(pl[p] >> 32), w1 % 64);
+            }
+        }
+    }
+
+    const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_local;
+    uint32_t* words = reinterpret_cast<uint32_t*>(pool + g.v_planes_off + tile * g.v_planes_stride) +
+                      (size_t)grp * 3 * D;
+#pragma unroll
+    for (int r = 0; r < WPL; ++r) words[64 * r + lane] = wv[r];
+    if (hl == 0 && valid) {
+        __half* norms = reinterpret_cast<__half*>(pool + g.v_norms_off + tile * g.v_norms_stride);
+        norms[token] = __float2half_rn(n);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_compress_k(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
@@ -199,9 +335,10 @@ hipError_t launch_compress_v(const void* v_fp16, uint8_t* pool, const PoolGeom& 
     const uint64_t waves = (items + 1) / 2;
     const uint32_t blocks = (uint32_t)((waves + 3) / 4);
     const __half* v = (const __half*)v_fp16;
+    const uint32_t mblocks = (uint32_t)((items + 3) / 4);  // one wave per 32-token group
     switch (g.head_dim) {
-        case 64: hipLaunchKernelGGL(k_compress_v<64>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items); break;
-        case 128: hipLaunchKernelGGL(k_compress_v<128>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items); break;
+        case 64: hipLaunchKernelGGL(k_compress_v_mfma<64>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items); break;
+        case 128: hipLaunchKernelGGL(k_compress_v_mfma<128>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items); break;
         case 256: hipLaunchKernelGGL(k_compress_v<256>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items); break;
         default: return hipErrorInvalidValue;
     }
