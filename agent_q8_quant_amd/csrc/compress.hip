@@ -18,6 +18,15 @@ namespace {
 // Keys. One thread owns 8 consecutive entries (one 16-B load); the 4 threads of a quad
 // own one 32-entry block and combine their |x| maxima through two lane exchanges.
 // Grid: x over 8-entry vectors of a tile, y over the tiles of the layer range.
+//
+// Arithmetic, equal to the definition (IEEE amax / 127, round-half-even of x / s):
+// - m / 127 for an fp16 m lies at least 1/254 of an fp16 ulp from every fp16 rounding
+//   midpoint, so amax * fl(1/127) (relative error < 2^-22) rounds to the same fp16 scale;
+// - x and s are fp16, so every quotient x / s that is not a tie lies at least 2^-13 from
+//   a half-integer, and a tie is exactly representable in fp32. The quotient below,
+//   t = x r with r = rcp(s), refined once by t + (x - t s) r, is within ~2^-40 relative
+//   of x / s: it equals the quotient whenever that is representable (every tie), and is
+//   far closer than 2^-13 otherwise, so rint gives round-half-even of the exact x / s.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_compress_k(const uint4* __restrict__ k,
                                                     uint8_t* __restrict__ pool, PoolGeom g,
@@ -40,16 +49,16 @@ __global__ __launch_bounds__(256) void k_compress_k(const uint4* __restrict__ k,
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
 
-    const float s32 = amax / 127.0f;            // IEEE float32 division
-    const __half s16 = __float2half_rn(s32);    // round to nearest even
+    const __half s16 = __float2half_rn(amax * (1.0f / 127.0f));   // = RNE16(amax / 127)
     const float s = __half2float(s16);
+    const float r = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;   // s = 0: every code 0
 
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        float q = 0.0f;
-        if (s != 0.0f) q = rintf(x[e] / s);     // exact division, half to even
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
+        const float t = x[e] * r;
+        const float t2 = __builtin_fmaf(__builtin_fmaf(-t, s, x[e]), r, t);
+        const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(t2), -127.0f, 127.0f);
         const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)q;
         packed[e >> 2] |= b << (8 * (e & 3));
     }

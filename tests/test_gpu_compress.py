@@ -47,6 +47,64 @@ def test_compress_full_config(cfg):
     _say("  value-code mismatches %d of %d" % (mism, coords))
 
 
+def _tie_blocks():
+    """q8_0 blocks holding every exact rounding tie x = (k + 1/2) s that fp16 can represent,
+    for every fp16 scale s that some fp16 block maximum produces, plus the fp16 neighbours
+    of each tie on both sides. Element 0 of a block is its maximum |x| (so it sets s)."""
+    s_all = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)
+    with np.errstate(over="ignore"):
+        base = (s_all.astype(np.float32) * np.float32(127)).astype(np.float16)
+    amax = np.full(len(s_all), np.nan, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        for off in (0, -1, 1, -2, 2):
+            cand = (base.view(np.uint16).astype(np.int32) + off).clip(1, 0x7BFF).astype(np.uint16).view(np.float16)
+            ok = np.isnan(amax) & np.isfinite(base) & \
+                ((cand.astype(np.float32) / np.float32(127)).astype(np.float16) == s_all)
+            amax[ok] = cand[ok].astype(np.float32)
+    keep = ~np.isnan(amax)
+    rows = []
+    kk = np.arange(127, dtype=np.float64) + 0.5
+    for sv, av in zip(s_all[keep].astype(np.float64), amax[keep].astype(np.float64)):
+        x = kk * sv
+        xh = x.astype(np.float16)
+        tie = xh[(xh.astype(np.float64) == x) & (x <= av)]
+        if tie.size == 0:
+            continue
+        up = np.nextafter(tie, np.float16(np.inf))
+        dn = np.nextafter(tie, np.float16(0))
+        vals = np.concatenate([tie, up[up.astype(np.float64) <= av], dn])
+        signs = np.where(np.arange(vals.size) % 2 == 0, 1, -1).astype(np.float16)
+        vals = vals * signs
+        for i in range(0, vals.size, 31):
+            blk = np.zeros(32, dtype=np.float16)
+            blk[0] = np.float16(av)
+            chunk = vals[i:i + 31]
+            blk[1:1 + chunk.size] = chunk
+            rows.append(blk)
+    return np.stack(rows)
+
+
+def test_k_codes_exact_at_every_representable_tie():
+    """Round-half-even of x / s at every exact tie (and next to it), bit-exact."""
+    blocks = _tie_blocks()
+    d = 128
+    nb = d // 32
+    T = (len(blocks) + nb - 1) // nb
+    kx = np.zeros((T * nb, 32), dtype=np.float16)
+    kx[:len(blocks)] = blocks
+    kx = kx.reshape(1, 1, T, d)
+    _say("tie blocks", len(blocks), "tokens", T)
+    lay = pk.polykv_pool_layout(1, 1, d, T)
+    pool = new_pool(lay)
+    pk.polykv_compress_k(torch.from_numpy(kx).to(device()), pool, lay)
+    torch.cuda.synchronize()
+    got = read_pool(pool, lay)
+    codes, scales = oracle.q8_0_encode(kx[0])
+    assert np.array_equal(got["k_scales"][0].view(np.uint16), scales[0].view(np.uint16))
+    bad = np.argwhere(got["k_codes"][0] != codes[0])
+    assert bad.size == 0, (len(bad), bad[:5])
+
+
 @pytest.mark.parametrize("T", [1, 31, 33, 100])
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_compress_ragged_and_dims(T, d):
