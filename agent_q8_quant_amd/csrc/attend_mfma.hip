@@ -90,7 +90,8 @@ struct MCfg {
     static constexpr int LUT_BYTES = 4096 * 8;
     static constexpr int OFF_LUT = 0;
     static constexpr int OFF_MASK = LUT_BYTES;                 // fp16 [2][CHUNK] token weights
-    static constexpr int OFF_STREAMS = OFF_MASK + 256;
+    static constexpr int OFF_PAIR = OFF_MASK + 256;            // fp16 [64][2] pair table
+    static constexpr int OFF_STREAMS = OFF_PAIR + 256;
     static constexpr int LDS = OFF_STREAMS + STREAMS * STREAM_BYTES;
     // DMA instructions per chunk
     static constexpr int K_INSTR = K_BYTES / 1024;
@@ -326,38 +327,42 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
                     for (int e = 0; e < 8; ++e) x[e] = 0.0f;
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = x[e] * qs;
-                    const _Float16 hi = (_Float16)v;
-                    qh[rb][b][e] = hi;
-                    ql[rb][b][e] = (_Float16)(v - (float)hi);
-                }
-            }
-        }
-    }
-
-    // value lookup table: entry e -> lambda * the centroids of the 4 tokens whose plane bits
-    // are the nibbles (e & 15, (e >> 4) & 15, e >> 8), in fp16
-    {
-        h4* lut = reinterpret_cast<h4*>(lds + C::OFF_LUT);
-        const float lam = a.cb.fp16_scale;
-        for (int e = tid; e < 4096; e += C::THREADS) {
-            h4 v;
+                for (int e = 0; e < 8; ++e) x[e] *= qs;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t code = ((e >> u) & 1) | (((e >> (4 + u)) & 1) << 1) | (((e >> (8 + u)) & 1) << 2);
-                v[u] = (_Float16)(lam * centroid_full(code, a.cb));
+                for (int e = 0; e < 8; ++e) qh[rb][b][e] = (_Float16)x[e];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ql[rb][b][e] = (_Float16)(x[e] - (float)qh[rb][b][e]);
             }
-            lut[e] = v;
         }
     }
 
+    // value lookup table, built in two steps. Pair table: entry x (6 bits: plane 0, 1 and 2
+    // bits of token A at bits 0, 2, 4 and of token B at bits 1, 3, 5) -> lambda * the
+    // centroids of A and B in fp16. Main table: entry e -> the centroids of the 4 tokens whose
+    // plane bits are the nibbles (e & 15, (e >> 4) & 15, e >> 8), i.e. two pair entries.
+    if (tid < 64) {
+        const float lam = a.cb.fp16_scale;
+        const uint32_t ca = (tid & 1) | (((tid >> 2) & 1) << 1) | (((tid >> 4) & 1) << 2);
+        const uint32_t cbb = ((tid >> 1) & 1) | (((tid >> 3) & 1) << 1) | (((tid >> 5) & 1) << 2);
+        reinterpret_cast<h2*>(lds + C::OFF_PAIR)[tid] =
+            h2{(_Float16)(lam * centroid_full(ca, a.cb)), (_Float16)(lam * centroid_full(cbb, a.cb))};
+    }
     // token weights of a full chunk (all 1) and of the tile's last chunk (1 below T)
     if (tid < 2 * CHUNK) {
         const int t = tid & (CHUNK - 1);
         const bool tail = tid >= CHUNK;
         reinterpret_cast<_Float16*>(lds + C::OFF_MASK)[tid] =
             (!tail || (NC - 1) * CHUNK + t < T) ? (_Float16)1.0f : (_Float16)0.0f;
+    }
+    __syncthreads();  // pair table complete
+    {
+        const uint32_t* pair = reinterpret_cast<const uint32_t*>(lds + C::OFF_PAIR);
+        uint2* lut = reinterpret_cast<uint2*>(lds + C::OFF_LUT);
+        for (int e = tid; e < 4096; e += C::THREADS) {
+            const uint32_t i01 = (e & 3) | ((e >> 2) & 0xC) | ((e >> 4) & 0x30);
+            const uint32_t i23 = ((e >> 2) & 3) | ((e >> 4) & 0xC) | ((e >> 6) & 0x30);
+            lut[e] = make_uint2(pair[i01], pair[i23]);
+        }
     }
     // start streaming NSK - 1 key chunks and NSV - 1 plane chunks ahead; the first key
     // chunk must have landed before the first barrier publishes it
