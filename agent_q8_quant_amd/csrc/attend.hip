@@ -20,6 +20,7 @@ namespace polykv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float centroid_of(uint32_t code, const CodebookHalf& cb) {
     // code >= 4: +c[code - 4] of the positive half; code <= 3: -c[3 - code]
@@ -44,7 +45,8 @@ struct ValuCfg {
     static constexpr int OFF_P = OFF_V + C * D;
     static constexpr int OFF_N = OFF_P + C * RP;
     static constexpr int OFF_L = OFF_N + C;
-    static constexpr int FLOATS = OFF_L + RP;
+    static constexpr int OFF_M = OFF_L + RP;
+    static constexpr int FLOATS = OFF_M + RP;
     static_assert(TPT >= 1 && DPT >= 1, "thread mapping");
     static_assert(RP * D <= D * C + C * D, "final accumulator must fit the K and V stages");
 };
@@ -61,6 +63,7 @@ __global__ __launch_bounds__(256) void k_attend_valu(AttendArgs a) {
     float* pT = lds + Cfg::OFF_P;   // [C][RP]   softmax numerators
     float* nrm = lds + Cfg::OFF_N;  // [C]       value norms
     float* lrow = lds + Cfg::OFF_L; // [RP]      row sums at the end
+    float* mrow = lds + Cfg::OFF_M; // [RP]      row maxima at the end (log2 units)
 
     const PoolGeom& g = a.g;
     const int tid = threadIdx.x;
@@ -217,7 +220,10 @@ __global__ __launch_bounds__(256) void k_attend_valu(AttendArgs a) {
         for (int e = 0; e < DPT; ++e) accs[(4 * rq + r) * D + tq * DPT + e] = acc[r][e];
     if (tq == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lrow[4 * rq + r] = l_run[r];
+        for (int r = 0; r < 4; ++r) {
+            lrow[4 * rq + r] = l_run[r];
+            mrow[4 * rq + r] = m_run[r];
+        }
     }
     __syncthreads();
     if (tid < R) {
@@ -237,6 +243,10 @@ __global__ __launch_bounds__(256) void k_attend_valu(AttendArgs a) {
         }
         const float inv = 1.0f / ((float)D * lrow[tid]);
         const int ag = tid / G, j = tid - ag * G;
+        // scores are in log2 units (scale * log2 e folded into q)
+        if (a.lse)
+            a.lse[((size_t)l_local * A + ag) * HG + (size_t)h * G + j] =
+                kLn2 * (mrow[tid] + __builtin_log2f(lrow[tid]));
         float* o = a.out + (((size_t)l_local * A + ag) * HG + (size_t)h * G + j) * D;
 #pragma unroll
         for (int i = 0; i < D; i += 4)

@@ -47,6 +47,7 @@ constexpr int CHUNK = 32;
 constexpr int NSK = 4;  // key ring depth (chunks)
 constexpr int NSV = 3;  // plane ring depth (chunks)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // log2 units a score may exceed the reference maximum
 
 constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -138,16 +139,25 @@ __device__ __forceinline__ void wait_chunks_after(int n) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // 8 int8 codes -> 8 fp16 (exact): sign-extending byte selects, two results per dword.
+// One asm block, because the compiler's hazard tracking does not look inside inline asm:
+// - a half-dword (dst_sel) write must not be read by the very next VALU instruction, so
+//   the four low-half writes come first and each high-half write (which reads the
+//   preserved low half) is four instructions behind its low-half write;
+// - a VALU result read by a matrix-core instruction needs two wait states, given by the
+//   closing s_nop 1 (the results feed v_mfma directly).
 __device__ __forceinline__ h8 codes_to_h8(uint2 raw) {
     uint32_t d0, d1, d2, d3;
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(d0) : "v"(raw.x));
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1" : "+v"(d0) : "v"(raw.x));
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(d1) : "v"(raw.x));
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(d1) : "v"(raw.x));
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(d2) : "v"(raw.y));
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1" : "+v"(d2) : "v"(raw.y));
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(d3) : "v"(raw.y));
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(d3) : "v"(raw.y));
+    asm("v_cvt_f16_i16_sdwa %0, sext(%4) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %1, sext(%4) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_f16_i16_sdwa %2, sext(%5) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %3, sext(%5) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%4) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+        "v_cvt_f16_i16_sdwa %1, sext(%4) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3\n\t"
+        "v_cvt_f16_i16_sdwa %2, sext(%5) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+        "v_cvt_f16_i16_sdwa %3, sext(%5) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3\n\t"
+        "s_nop 1"
+        : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+        : "v"(raw.x), "v"(raw.y));
     const uint4 u = make_uint4(d0, d1, d2, d3);
     return __builtin_bit_cast(h8, u);
 }
@@ -667,6 +677,10 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
         if (row < R) {
             const float inv = 1.0f / ((float)D * L * a.cb.fp16_scale);
             const int ag = row / G, jj = row - ag * G;
+            // scores are in log2 units and every p carries 2^-(m + slack)
+            if (a.lse && qtr == 0)
+                a.lse[((size_t)l_local * A + ag) * HG + (size_t)h * G + jj] =
+                    kLn2 * (M + kSlack + __builtin_log2f(L));
             float* o = a.out + (((size_t)l_local * A + ag) * HG + (size_t)h * G + jj) * D + qtr * QD;
 #pragma unroll
             for (int e = 0; e < QD; e += 4)

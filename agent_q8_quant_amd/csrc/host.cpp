@@ -265,12 +265,13 @@ size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_ag
                                           resolve_path(g, rows, POLYKV_PATH_AUTO));
 }
 
-int polykv_attend_shared_path(const void* pool, const polykv_layout_t* layout,
-                              const polykv_codebook_t* cb, const float* q, float* out,
-                              int32_t n_agents, int32_t gqa, float softmax_scale,
-                              int32_t layer_begin, int32_t layer_count, void* workspace,
-                              size_t workspace_bytes, void* hip_stream, int32_t path) {
+int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
+                             const polykv_codebook_t* cb, const float* q, float* out,
+                             float* lse, int32_t n_agents, int32_t gqa, float softmax_scale,
+                             int32_t layer_begin, int32_t layer_count, void* workspace,
+                             size_t workspace_bytes, void* hip_stream, int32_t path) {
     if (!pool || !layout || !q || !out) return POLYKV_ERR_NULL;
+    if (lse && !aligned(lse, 4)) return POLYKV_ERR_ALIGN;
     int rc = check_layout(layout);
     if (rc) return rc;
     if (n_agents < 1 || gqa < 1) return POLYKV_ERR_SHAPE;
@@ -295,6 +296,7 @@ int polykv_attend_shared_path(const void* pool, const polykv_layout_t* layout,
     a.cb = half_of(book);
     a.q = q;
     a.out = out;
+    a.lse = lse;
     a.n_agents = n_agents;
     a.gqa = gqa;
     a.layer_begin = layer_begin;
@@ -305,6 +307,51 @@ int polykv_attend_shared_path(const void* pool, const polykv_layout_t* layout,
     hipStream_t s = (hipStream_t)hip_stream;
     return launch_rc(path == POLYKV_PATH_MFMA ? polykv::launch_attend_mfma(a, s)
                                               : polykv::launch_attend_valu(a, s));
+}
+
+int polykv_attend_shared_path(const void* pool, const polykv_layout_t* layout,
+                              const polykv_codebook_t* cb, const float* q, float* out,
+                              int32_t n_agents, int32_t gqa, float softmax_scale,
+                              int32_t layer_begin, int32_t layer_count, void* workspace,
+                              size_t workspace_bytes, void* hip_stream, int32_t path) {
+    return polykv_attend_shared_lse(pool, layout, cb, q, out, nullptr, n_agents, gqa,
+                                    softmax_scale, layer_begin, layer_count, workspace,
+                                    workspace_bytes, hip_stream, path);
+}
+
+int polykv_attend_tail_merge(const polykv_layout_t* layout, const float* q, float* out,
+                             float* lse, const void* tail_k, const void* tail_v,
+                             const int32_t* tail_len, int32_t tail_cap, int32_t n_agents,
+                             int32_t gqa, float softmax_scale, int32_t layer_count,
+                             void* hip_stream) {
+    if (!layout || !q || !out || !lse || !tail_len) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (n_agents < 1 || gqa < 1 || tail_cap < 0) return POLYKV_ERR_SHAPE;
+    if ((int64_t)n_agents * gqa > POLYKV_MAX_ROWS) return POLYKV_ERR_RANGE;
+    if (layer_count < 1 || layer_count > layout->shape.n_layers) return POLYKV_ERR_RANGE;
+    if (!std::isfinite(softmax_scale)) return POLYKV_ERR_ARG;
+    if (tail_cap > 0 && (!tail_k || !tail_v)) return POLYKV_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(tail_len, 4))
+        return POLYKV_ERR_ALIGN;
+    if (tail_cap > 0 && (!aligned(tail_k, 16) || !aligned(tail_v, 16))) return POLYKV_ERR_ALIGN;
+    if (tail_cap == 0) return POLYKV_OK;  // no tail tokens: the pool result stands
+    if ((rc = check_device())) return rc;
+    polykv::TailArgs a;
+    a.q = q;
+    a.out = out;
+    a.lse = lse;
+    a.tail_k = tail_k;
+    a.tail_v = tail_v;
+    a.tail_len = tail_len;
+    a.tail_cap = tail_cap;
+    a.n_kv_heads = layout->shape.n_kv_heads;
+    a.head_dim = layout->shape.head_dim;
+    a.gqa = gqa;
+    a.n_agents = n_agents;
+    a.layer_count = layer_count;
+    a.softmax_scale = softmax_scale;
+    return launch_rc(polykv::launch_attend_tail(a, (hipStream_t)hip_stream));
 }
 
 int polykv_attend_shared(const void* pool, const polykv_layout_t* layout,

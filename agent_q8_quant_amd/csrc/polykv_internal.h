@@ -58,11 +58,26 @@ struct AttendArgs {
     CodebookHalf cb;
     const float* q;
     float* out;
+    float* lse;  // optional [layer_count][n_agents][H * gqa]: ln sum_t exp(scale q . k_t)
     int32_t n_agents, gqa, layer_begin, layer_count;
     float softmax_scale;
     void* workspace;
     size_t workspace_bytes;
 };
+
+// Private-tail merge (attend_tail.hip).
+struct TailArgs {
+    const float* q;
+    float* out;   // in: shared-pool result, out: merged result
+    float* lse;   // in/out, natural log
+    const void* tail_k;
+    const void* tail_v;
+    const int32_t* tail_len;
+    int32_t tail_cap;
+    int32_t n_kv_heads, head_dim, gqa, n_agents, layer_count;
+    float softmax_scale;
+};
+hipError_t launch_attend_tail(const TailArgs& a, hipStream_t s);
 
 size_t attend_workspace_bytes(const PoolGeom& g, int32_t n_agents, int32_t gqa,
                               int32_t layer_count, int32_t path);

@@ -20,7 +20,7 @@ POLYKV_MAX_ROWS = 64
 EXPORTED_SYMBOLS = (
     "polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k", "polykv_compress_v",
     "polykv_attend_workspace_bytes", "polykv_attend_path", "polykv_attend_shared", "polykv_attend_shared_path",
-    "polykv_strerror",
+    "polykv_attend_shared_lse", "polykv_attend_tail_merge", "polykv_strerror",
 )
 
 
@@ -72,10 +72,14 @@ def lib():
                i32, i32, ctypes.c_float, i32, i32, vp, sz, vp]
         L.polykv_attend_shared.argtypes = att
         L.polykv_attend_shared_path.argtypes = att + [i32]
+        L.polykv_attend_shared_lse.argtypes = att[:5] + [vp] + att[5:] + [i32]
+        L.polykv_attend_tail_merge.argtypes = [ctypes.POINTER(polykv_layout_t), vp, vp, vp, vp, vp, vp,
+                                               i32, i32, i32, ctypes.c_float, i32, vp]
         L.polykv_strerror.argtypes = [ctypes.c_int]
         L.polykv_strerror.restype = ctypes.c_char_p
         for name in ("polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k",
-                     "polykv_compress_v", "polykv_attend_shared", "polykv_attend_shared_path"):
+                     "polykv_compress_v", "polykv_attend_shared", "polykv_attend_shared_path",
+                     "polykv_attend_shared_lse", "polykv_attend_tail_merge"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -158,24 +162,57 @@ def polykv_attend_path(layout, n_agents, gqa) -> int:
     return rc
 
 
-def polykv_attend_shared_path(pool, layout, q, out, n_agents, gqa, softmax_scale, path,
-                              layer_begin=0, layer_count=None, cb=None, workspace=None,
-                              stream=None):
+def polykv_attend_shared_lse(pool, layout, q, out, lse, n_agents, gqa, softmax_scale,
+                             path=POLYKV_PATH_AUTO, layer_begin=0, layer_count=None, cb=None,
+                             workspace=None, stream=None):
     lb, lc = _layers(layout, layer_begin, layer_count)
     s = layout.shape
     n = lc * n_agents * s.n_kv_heads * gqa * s.head_dim
     if q.numel() != n or out.numel() != n or pool.numel() < layout.total_bytes:
         raise ValueError("q, out or pool has the wrong size")
+    lse_ptr = None
+    if lse is not None:
+        if lse.numel() != n // s.head_dim:
+            raise ValueError("lse has the wrong size")
+        lse_ptr = _dev(lse, torch.float32, "lse")
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, torch.uint8, "workspace"), workspace.numel()
-    rc = lib().polykv_attend_shared_path(
+    rc = lib().polykv_attend_shared_lse(
         _dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
         ctypes.byref(cb) if cb is not None else None,
-        _dev(q, torch.float32, "q"), _dev(out, torch.float32, "out"),
+        _dev(q, torch.float32, "q"), _dev(out, torch.float32, "out"), lse_ptr,
         int(n_agents), int(gqa), float(softmax_scale), lb, lc, ws_ptr, ws_bytes,
         _stream_ptr(stream), int(path))
-    _check(rc, "polykv_attend_shared")
+    _check(rc, "polykv_attend_shared_lse")
+
+
+def polykv_attend_shared_path(pool, layout, q, out, n_agents, gqa, softmax_scale, path,
+                              layer_begin=0, layer_count=None, cb=None, workspace=None,
+                              stream=None):
+    polykv_attend_shared_lse(pool, layout, q, out, None, n_agents, gqa, softmax_scale, path,
+                             layer_begin, layer_count, cb, workspace, stream)
+
+
+def polykv_attend_tail_merge(layout, q, out, lse, tail_k, tail_v, tail_len, n_agents, gqa,
+                             softmax_scale, layer_count=None, stream=None):
+    lc = layout.shape.n_layers if layer_count is None else int(layer_count)
+    s = layout.shape
+    n = lc * n_agents * s.n_kv_heads * gqa * s.head_dim
+    if q.numel() != n or out.numel() != n or lse.numel() != n // s.head_dim:
+        raise ValueError("q, out or lse has the wrong size")
+    if tail_k.shape != tail_v.shape or tail_k.dim() != 5 or tail_k.shape[:3] != (n_agents, lc, s.n_kv_heads) \
+            or tail_k.shape[4] != s.head_dim or tail_len.numel() != n_agents:
+        raise ValueError("tail_k, tail_v or tail_len has the wrong shape")
+    cap = int(tail_k.shape[3])
+    rc = lib().polykv_attend_tail_merge(
+        ctypes.byref(layout), _dev(q, torch.float32, "q"), _dev(out, torch.float32, "out"),
+        _dev(lse, torch.float32, "lse"),
+        _dev(tail_k, torch.float16, "tail_k") if cap else None,
+        _dev(tail_v, torch.float16, "tail_v") if cap else None,
+        _dev(tail_len, torch.int32, "tail_len"), cap, int(n_agents), int(gqa),
+        float(softmax_scale), lc, _stream_ptr(stream))
+    _check(rc, "polykv_attend_tail_merge")
 
 
 def polykv_attend_shared(pool, layout, q, out, n_agents, gqa, softmax_scale, layer_begin=0,

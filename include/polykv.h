@@ -171,6 +171,46 @@ int polykv_attend_shared_path(const void* pool, const polykv_layout_t* layout,
                               void* workspace, size_t workspace_bytes, void* hip_stream,
                               int32_t path);
 
+/*
+ * As polykv_attend_shared_path, and also the log-sum-exp of every output row:
+ *  lse: device fp32 [layer_count][n_agents][n_kv_heads * gqa] (4-B aligned) or NULL;
+ *       lse = ln sum_t exp(softmax_scale * q . k_hat_t) over the pool's tokens, the
+ *       quantity that merges this result with attention over other tokens.
+ * Errors: as polykv_attend_shared_path.
+ */
+int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
+                             const polykv_codebook_t* cb, const float* q, float* out,
+                             float* lse, int32_t n_agents, int32_t gqa, float softmax_scale,
+                             int32_t layer_begin, int32_t layer_count,
+                             void* workspace, size_t workspace_bytes, void* hip_stream,
+                             int32_t path);
+
+/*
+ * Private tails. PolyKV, Abstract: the one compressed pool is handed to N separate agent
+ * contexts, each of which goes on by itself; the tokens an agent adds after the pool was
+ * written are its own, kept uncompressed. This call attends every query row over its
+ * agent's tail and merges that with the shared-pool result, so that out becomes softmax
+ * attention over the union of pool and tail tokens:
+ *   M = max(lse_p, lse_t), w_p = exp(lse_p - M), w_t = exp(lse_t - M),
+ *   out = (w_p out_p + w_t out_t) / (w_p + w_t),  lse = M + ln(w_p + w_t).
+ *  layout:  supplies n_kv_heads and head_dim (the pool itself is not read).
+ *  q:       device fp32 [layer_count][n_agents][n_kv_heads * gqa][head_dim], 16-B aligned,
+ *           the same queries the pool result was computed for.
+ *  out, lse: device, in: the result of polykv_attend_shared_lse for q; out: the merged
+ *           result (rows of an agent with an empty tail are left as they are).
+ *  tail_k, tail_v: device fp16 [n_agents][layer_count][n_kv_heads][tail_cap][head_dim],
+ *           16-B aligned; query head j of an agent reads KV head j / gqa of its own tail.
+ *  tail_len: device int32 [n_agents]; agent a uses tail tokens [0, tail_len[a]); values
+ *           outside [0, tail_cap] are clamped into it.
+ *  tail_cap = 0 returns POLYKV_OK without any device work (tail_k, tail_v may be NULL).
+ * Errors: NULL, SHAPE, ALIGN, RANGE, LAYOUT, ARG, DEVICE, LAUNCH.
+ */
+int polykv_attend_tail_merge(const polykv_layout_t* layout, const float* q, float* out,
+                             float* lse, const void* tail_k, const void* tail_v,
+                             const int32_t* tail_len, int32_t tail_cap, int32_t n_agents,
+                             int32_t gqa, float softmax_scale, int32_t layer_count,
+                             void* hip_stream);
+
 /* Static English text for a return code. Never NULL. */
 const char* polykv_strerror(int code);
 

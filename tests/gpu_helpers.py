@@ -123,3 +123,19 @@ def row_rel_err(out, ref):
     num = np.max(np.abs(out - ref), axis=-1)
     den = np.max(np.abs(ref), axis=-1)
     return float(np.max(num / den))
+
+
+def oracle_pool_on_device(L, H, d, T, seed, k_scale=1.0):
+    """The oracle's pool of seeded N(0,1) K/V (K optionally scaled), uploaded as the
+    library's byte image; returns (layout, device pool, k_hat, v_hat) with the oracle's
+    fp64 per-token reconstructions [L][H][T][d]."""
+    rng = np.random.default_rng(seed)
+    kx = (rng.standard_normal((L, H, T, d)) * k_scale).astype(np.float16)
+    vx = rng.standard_normal((L, H, T, d)).astype(np.float16)
+    lay = pk.polykv_pool_layout(L, H, d, T)
+    op = oracle.compress_pool(kx, vx, B32)
+    tiles = L * H
+    img = pool_from_arrays(lay, op["k_codes"].reshape(tiles, T, d), op["k_scales"].reshape(tiles, T, d // 32),
+                           op["v_planes"].reshape(tiles, -1, 3, d), op["v_norms"].reshape(tiles, T))
+    kh, vh = oracle.dequant_pool(op, C32)
+    return lay, torch.from_numpy(img).to(device()), kh, vh

@@ -198,6 +198,23 @@ def test_ragged_tokens_and_rows(T, rows, path):
 
 
 @pytest.mark.parametrize("path", PATHS, ids=["valu", "mfma"])
+@pytest.mark.parametrize("T", [1, 32, 95, 300])
+@pytest.mark.parametrize("rows", [(1, 1), (5, 1), (3, 4), (17, 1), (16, 4)])
+def test_ragged_tokens_and_rows_head_dim_64(T, rows, path):
+    """head_dim 64 has its own matrix-core instantiations (one, two and four 16-row blocks)."""
+    _supported(path, CONFIGS[0])
+    A, G = rows
+    H, d = 3, 64
+    lay, pool, kh, vh = _tiny_pool(T, d=d, H=H, seed=T + 64)
+    qn = np.random.default_rng(T + 11).standard_normal((1, A, H * G, d)).astype(np.float32)
+    q = torch.from_numpy(qn).to(device())
+    out = torch.full_like(q, float("nan"))
+    pk.polykv_attend_shared_path(pool, lay, q, out, A, G, d ** -0.5, path)
+    ref = oracle.shared_pool_decode(qn, kh, vh, G, d ** -0.5)
+    assert row_rel_err(out.cpu().numpy(), ref) <= DECODE_REL_TOL
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["valu", "mfma"])
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_head_dims(d, path):
     _supported(path, CONFIGS[0])

@@ -149,6 +149,29 @@ def test_attend_path_choice(L):
     assert L.polykv_attend_path(ctypes.byref(bad), 1, 1) == -9
 
 
+def test_tail_merge_validation(L):
+    lay = _layout()
+    vp = ctypes.c_void_p
+    dev = vp(0x100000)
+    args = dict(q=dev, out=dev, lse=dev, tk=dev, tv=dev, tl=dev, cap=8, A=2, G=2, scale=0.1, lc=2)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.polykv_attend_tail_merge(ctypes.byref(lay), a["q"], a["out"], a["lse"], a["tk"], a["tv"],
+                                          a["tl"], a["cap"], a["A"], a["G"], ctypes.c_float(a["scale"]),
+                                          a["lc"], None)
+    assert call(q=None) == -1
+    assert call(tl=None) == -1
+    assert call(tk=None) == -1          # a non-empty tail needs its buffers
+    assert call(A=0) == -2
+    assert call(cap=-1) == -2
+    assert call(A=17, G=4) == -4
+    assert call(lc=3) == -4             # more layers than the layout holds
+    assert call(scale=float("nan")) == -10
+    assert call(q=vp(0x100004)) == -3
+    assert call(cap=0, tk=None, tv=None) == 0   # nothing to merge: no device work at all
+
+
 def test_strerror(L):
     for code in range(0, -11, -1):
         assert isinstance(pk.polykv_strerror(code), str) and pk.polykv_strerror(code)
