@@ -43,6 +43,8 @@ def _parse():
     p.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
     p.add_argument("--warm", action="store_true", help="one pool copy, left in the caches between launches")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--tail-tokens", type=int, default=None,
+                   help="private fp16 tail per agent for the tail-merge figure (default: the decode steps)")
     p.add_argument("--cpu-sample-layers", type=int, default=None)
     p.add_argument("--mode", choices=["bench", "profile", "copy"], default="bench",
                    help="profile: a few launches for rocprofv3 and no JSON; copy: a 1 GiB device copy "
@@ -170,6 +172,17 @@ def main():
     n_pools = 1 if args.warm else 3
     pools = [torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev) for _ in range(n_pools)]
     stream = torch.cuda.Stream(device=dev)
+    # Private tails for the tail-merge figure: every agent's own fp16 K/V after n_tail
+    # decode steps, [agent][layer][kv head][token][dim]; copies used in turn like the pools.
+    n_tail = args.tail_tokens if args.tail_tokens is not None else D
+    tail_shape = (cfg.n_agents, cfg.n_layers, cfg.n_kv_heads, n_tail, cfg.head_dim)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260427)
+    tails = [(torch.randn(tail_shape, generator=gen, dtype=torch.float16, device=dev),
+              torch.randn(tail_shape, generator=gen, dtype=torch.float16, device=dev))
+             for _ in range(n_pools)] if n_tail > 0 else []
+    tail_len = torch.full((cfg.n_agents,), n_tail, dtype=torch.int32, device=dev)
+    lse = torch.empty((cfg.n_layers, cfg.n_agents, cfg.n_q_heads), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def ev():
@@ -196,10 +209,20 @@ def main():
             e.append(ev())
         rec.append(e)
 
+    def tail_merge(i):
+        tk, tv = tails[i % len(tails)]
+        pk.polykv_attend_tail_merge(lay, q[0], out, lse, tk, tv, tail_len, cfg.n_agents, cfg.gqa,
+                                    cfg.softmax_scale, stream=stream)
+
     with torch.cuda.stream(stream):
         if args.mode == "profile":
             for j in range(n_pools + max(1, args.steps)):
                 one_step(j, [])
+            if tails:
+                pk.polykv_attend_shared_lse(pools[0], lay, q[0], out, lse, cfg.n_agents, cfg.gqa,
+                                            cfg.softmax_scale, path, workspace=ws, stream=stream)
+                for i in range(2 * n_pools):
+                    tail_merge(i)
             stream.synchronize()
             print("profile run done: %d steps x (2 compress + %d decode) launches"
                   % (n_pools + args.steps, D), flush=True)
@@ -230,6 +253,19 @@ def main():
             stream.synchronize()
             cold_us = [a.elapsed_time(b) * 1e3 for a, b in cold_us]
             del flush
+
+        # Secondary figure: the private-tail merge after the pool decode (lse exported).
+        tail_ev = []
+        if tails:
+            pk.polykv_attend_shared_lse(pools[0], lay, q[0], out, lse, cfg.n_agents, cfg.gqa,
+                                        cfg.softmax_scale, path, workspace=ws, stream=stream)
+            for i in range(n_pools + 16):
+                e0 = ev()
+                tail_merge(i)
+                e1 = ev()
+                if i >= n_pools:
+                    tail_ev.append((e0, e1))
+            stream.synchronize()
 
     step_ms = [r[0].elapsed_time(r[-1]) for r in rec]
     ck_ms = [r[0].elapsed_time(r[1]) for r in rec]
@@ -283,6 +319,17 @@ def main():
     }
     if cold_us:
         result["decode_us_after_1GiB_write"] = cold_us
+    if tail_ev:
+        t_tail = sum(a.elapsed_time(b) for a, b in tail_ev) / len(tail_ev) / 1e3
+        # fp16 tail K and V, q read, out read + written, lse read + written
+        lse_bytes = cfg.n_layers * cfg.n_agents * cfg.n_q_heads * 4
+        tail_bytes = 2 * 2 * cfg.n_agents * cfg.n_layers * cfg.n_kv_heads * n_tail * cfg.head_dim \
+            + 3 * q_bytes + 2 * lse_bytes
+        result["tail_merge"] = {"kernel": "attend_tail", "tail_tokens_per_agent": n_tail,
+                                "us": t_tail * 1e6, "GBps": tail_bytes / t_tail / 1e9,
+                                "frac_hbm": tail_bytes / t_tail / 1e9 / HBM_PEAK_GBPS,
+                                "algorithmic_bytes_per_launch": tail_bytes,
+                                "traffic": _traffic("attend_tail", ["attend_tail.hip"], "%s_tail%d" % (workload, n_tail))}
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         n = args.cpu_sample_layers or cfg.n_layers
