@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpolykv.so")
-SOURCES = ["host.cpp", "compress.hip", "attend.hip", "attend_mfma.hip", "attend_tail.hip"]
+SOURCES = ["host.cpp", "compress.hip", "attend.hip", "attend_mfma.hip", "attend_tail.hip", "dequant.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU instructions in device code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

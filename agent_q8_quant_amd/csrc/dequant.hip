@@ -1,0 +1,199 @@
+// Dequantisation of the shared pool back to fp16 K and V (gfx950), the form a model's
+// ordinary KV cache holds.
+//
+// PolyKV abstract: keys are held as int8 q8_0 and values as TurboQuant MSE codes; the
+// integration on the pages hands the decompressed cache to the model as an ordinary
+// per-layer cache. Reconstruction, per token-head:
+// - key:   k_hat = code * s (the stored fp16 block scale), rounded once to fp16. The
+//          product of an int8 code and an fp16 scale is exact in fp32, so the result is
+//          the correctly rounded fp16 of the exact reconstruction;
+// - value: v_hat = (n / d) * H c[code] with n the stored fp16 norm, c the codebook's
+//          centroids and H the +-1 Sylvester matrix (the inverse of y = H v / ||v||; H is
+//          symmetric and H H = d I). The transform runs in fp32 (error far below one fp16
+//          ulp), then one rounding to fp16.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "polykv_internal.h"
+
+namespace polykv {
+namespace {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------------------
+// Keys: one thread per 8 consecutive entries (8 codes in, one 16-byte fp16 store out).
+// Grid: x over the 8-entry pieces of a tile, y over the tiles of the layer range.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dequant_k(const uint8_t* __restrict__ pool, PoolGeom g,
+                                                   int32_t layer_begin, uint32_t vec_per_tile,
+                                                   u4* __restrict__ out) {
+    const uint32_t tile_local = blockIdx.y;
+    const uint32_t v = blockIdx.x * 256u + threadIdx.x;
+    if (v >= vec_per_tile) return;
+    const uint32_t D = (uint32_t)g.head_dim;
+    const uint32_t per_row = D / 8;
+    const uint32_t t = v / per_row, c8 = v - t * per_row;
+    const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_local;
+    const uint8_t* codes = pool + g.k_codes_off + tile * g.k_codes_stride + (size_t)t * D + 8 * c8;
+    const __half* scales = reinterpret_cast<const __half*>(pool + g.k_scales_off + tile * g.k_scales_stride);
+    const uint2 raw = *reinterpret_cast<const uint2*>(codes);
+    const float s = __half2float(scales[(size_t)t * (D / 32) + c8 / 4]);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t word = e < 2 ? raw.x : raw.y;
+        const int8_t lo = (int8_t)((word >> (16 * (e & 1))) & 0xFFu);
+        const int8_t hi = (int8_t)((word >> (16 * (e & 1) + 8)) & 0xFFu);
+        const __half a = __float2half_rn((float)lo * s), b = __float2half_rn((float)hi * s);
+        w[e] = (uint32_t)__half_as_ushort(a) | ((uint32_t)__half_as_ushort(b) << 16);
+    }
+    out[(size_t)tile_local * vec_per_tile + v] = u4{w[0], w[1], w[2], w[3]};
+}
+
+// ---------------------------------------------------------------------------------------
+// Values: one wave per item. For head_dim 128 and 256 an item is one 32-token group of a
+// tile and lane l holds token l % 32, coordinates (l / 32) * d/2 .. + d/2 - 1; for
+// head_dim 64 an item is two consecutive groups and lane l holds token l % 32 of group
+// l / 32, all 64 coordinates. Steps:
+// 1. the item's plane words (3 x d per group) are staged in LDS, one copy per wave;
+// 2. lane l reads, per coordinate, the three words of its half and takes bit l % 32 of
+//    each: the code, whose centroid comes from an 8-entry LDS table;
+// 3. the FWHT runs in registers over the lane's coordinates, and for d >= 128 one last
+//    butterfly pairs lane l with lane l ^ 32 (the other coordinate half);
+// 4. times n / d, rounded to fp16, stored as 16-byte pieces.
+// ---------------------------------------------------------------------------------------
+template <int D>
+struct DqCfg {
+    static constexpr int HALVES = D == 64 ? 1 : 2;   // lanes per token
+    static constexpr int CPL = D / HALVES;           // coordinates per lane
+    static constexpr int GPW = D == 64 ? 2 : 1;      // groups per wave
+    static constexpr int WORDS = GPW * 3 * D;        // plane words per item
+    static constexpr int WAVE_LDS = WORDS * 4;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ pool, PoolGeom g,
+                                                   CodebookHalf cb, int32_t layer_begin,
+                                                   uint32_t items_per_tile, uint32_t n_items,
+                                                   __half* __restrict__ out) {
+    using C = DqCfg<D>;
+    constexpr int CPL = C::CPL;
+    __shared__ __attribute__((aligned(16))) uint32_t words[4][C::WORDS];
+    __shared__ float ctab[8];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid < 8) {
+        const int m = tid >= 4 ? tid - 4 : 3 - tid;
+        const float mag = m == 0 ? cb.centroid_pos[0] : m == 1 ? cb.centroid_pos[1]
+                        : m == 2 ? cb.centroid_pos[2] : cb.centroid_pos[3];
+        ctab[tid] = tid >= 4 ? mag : -mag;
+    }
+    __syncthreads();  // the only workgroup barrier: waves without an item leave after it
+    const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4u + (uint32_t)w));
+    if (item >= n_items) return;
+    const uint32_t tile_local = item / items_per_tile;
+    const uint32_t gi = item - tile_local * items_per_tile;
+    const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_local;
+    const int T = g.n_tokens;
+    const int g0 = (int)gi * C::GPW;                       // first group of the item
+    const int n_grp = min(C::GPW, g.n_groups - g0);        // groups present (1 or GPW)
+
+    // 1. stage the plane words: [group][plane][d] as stored
+    const u4* src = reinterpret_cast<const u4*>(pool + g.v_planes_off + tile * g.v_planes_stride +
+                                                (size_t)g0 * (3 * D * 4));
+    u4* dst = reinterpret_cast<u4*>(&words[w][0]);
+    for (int i = lane; i < n_grp * 3 * D / 4; i += 64) dst[i] = src[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const int half = lane >> 5, t = lane & 31;
+    const int grp = C::GPW == 2 ? g0 + half : g0;
+    const int coord0 = C::GPW == 2 ? 0 : half * CPL;
+    const int token = 32 * grp + t;
+    const bool valid = token < T && (C::GPW == 1 || half < n_grp);
+    const uint32_t* wb = &words[w][(C::GPW == 2 ? half * 3 * D : 0) + coord0];
+
+    // 2. codes -> centroids
+    float x[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c += 4) {
+        const u4 p0 = *reinterpret_cast<const u4*>(wb + c);
+        const u4 p1 = *reinterpret_cast<const u4*>(wb + D + c);
+        const u4 p2 = *reinterpret_cast<const u4*>(wb + 2 * D + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t code = __builtin_amdgcn_ubfe(p0[e], t, 1) | (__builtin_amdgcn_ubfe(p1[e], t, 1) << 1) |
+                                  (__builtin_amdgcn_ubfe(p2[e], t, 1) << 2);
+            x[c + e] = ctab[code];
+        }
+    }
+    // 3. Sylvester FWHT over the lane's coordinates (pairs at distance h become (a+b, a-b))
+#pragma unroll
+    for (int h = 1; h < CPL; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+            if (!(e & h)) {
+                const float a = x[e], b = x[e + h];
+                x[e] = a + b;
+                x[e + h] = a - b;
+            }
+    if constexpr (C::HALVES == 2) {
+        // coordinate bit log2(d/2): lower half (a) and upper half (b) of the same token
+        const float sgn = half ? -1.0f : 1.0f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            const uint32_t u = __float_as_uint(x[e]);
+            const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            // s[0]: the lower half's value in every lane, s[1]: the upper half's
+            x[e] = __builtin_fmaf(sgn, __uint_as_float(s[1]), __uint_as_float(s[0]));
+        }
+    }
+    if (!valid) return;
+    // 4. scale by n / d and store
+    const __half* norms = reinterpret_cast<const __half*>(pool + g.v_norms_off + tile * g.v_norms_stride);
+    const float f = __half2float(norms[token]) * (1.0f / (float)D);
+    u4* o = reinterpret_cast<u4*>(out + ((size_t)tile_local * T + token) * D + coord0);
+#pragma unroll
+    for (int c = 0; c < CPL; c += 8) {
+        uint32_t q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            q[e] = (uint32_t)__half_as_ushort(__float2half_rn(x[c + 2 * e] * f)) |
+                   ((uint32_t)__half_as_ushort(__float2half_rn(x[c + 2 * e + 1] * f)) << 16);
+        o[c / 8] = u4{q[0], q[1], q[2], q[3]};
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dequant_k(const uint8_t* pool, void* k_fp16, const PoolGeom& g,
+                            int32_t layer_begin, int32_t layer_count, hipStream_t s) {
+    const uint32_t vec_per_tile = (uint32_t)((uint64_t)g.n_tokens * g.head_dim / 8);
+    const uint32_t tiles = (uint32_t)layer_count * (uint32_t)g.n_kv_heads;
+    dim3 grid((vec_per_tile + 255) / 256, tiles);
+    hipLaunchKernelGGL(k_dequant_k, grid, dim3(256), 0, s, pool, g, layer_begin, vec_per_tile,
+                       (u4*)k_fp16);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_v(const uint8_t* pool, void* v_fp16, const PoolGeom& g,
+                            const CodebookHalf& cb, int32_t layer_begin, int32_t layer_count,
+                            hipStream_t s) {
+    const uint32_t gpw = g.head_dim == 64 ? 2u : 1u;
+    const uint32_t items_per_tile = ((uint32_t)g.n_groups + gpw - 1) / gpw;
+    const uint64_t items = (uint64_t)layer_count * g.n_kv_heads * items_per_tile;
+    const uint32_t blocks = (uint32_t)((items + 3) / 4);
+    __half* out = (__half*)v_fp16;
+    switch (g.head_dim) {
+        case 64: hipLaunchKernelGGL(k_dequant_v<64>, dim3(blocks), dim3(256), 0, s, pool, g, cb, layer_begin, items_per_tile, (uint32_t)items, out); break;
+        case 128: hipLaunchKernelGGL(k_dequant_v<128>, dim3(blocks), dim3(256), 0, s, pool, g, cb, layer_begin, items_per_tile, (uint32_t)items, out); break;
+        case 256: hipLaunchKernelGGL(k_dequant_v<256>, dim3(blocks), dim3(256), 0, s, pool, g, cb, layer_begin, items_per_tile, (uint32_t)items, out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace polykv

@@ -238,6 +238,33 @@ int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* lay
                                                (hipStream_t)hip_stream));
 }
 
+int polykv_dequant_k(const void* pool, const polykv_layout_t* layout, void* k_fp16,
+                     int32_t layer_begin, int32_t layer_count, void* hip_stream) {
+    if (!pool || !layout || !k_fp16) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (!aligned(pool, 256) || !aligned(k_fp16, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_dequant_k((const uint8_t*)pool, k_fp16, polykv::make_geom(*layout),
+                                              layer_begin, layer_count, (hipStream_t)hip_stream));
+}
+
+int polykv_dequant_v(const void* pool, const polykv_layout_t* layout, const polykv_codebook_t* cb,
+                     void* v_fp16, int32_t layer_begin, int32_t layer_count, void* hip_stream) {
+    if (!pool || !layout || !v_fp16) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (!aligned(pool, 256) || !aligned(v_fp16, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
+    const polykv_codebook_t& book = cb ? *cb : default_codebook();
+    if (!codebook_ok(book)) return POLYKV_ERR_CODEBOOK;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_dequant_v((const uint8_t*)pool, v_fp16, polykv::make_geom(*layout),
+                                              half_of(book), layer_begin, layer_count,
+                                              (hipStream_t)hip_stream));
+}
+
 static int resolve_path(const polykv::PoolGeom& g, int32_t rows, int32_t path) {
     if (path == POLYKV_PATH_AUTO)
         return polykv::attend_mfma_supported(g, rows) && rows > 16 ? POLYKV_PATH_MFMA

@@ -79,6 +79,13 @@ struct TailArgs {
 };
 hipError_t launch_attend_tail(const TailArgs& a, hipStream_t s);
 
+// Pool -> fp16 K / V (dequant.hip).
+hipError_t launch_dequant_k(const uint8_t* pool, void* k_fp16, const PoolGeom& g,
+                            int32_t layer_begin, int32_t layer_count, hipStream_t s);
+hipError_t launch_dequant_v(const uint8_t* pool, void* v_fp16, const PoolGeom& g,
+                            const CodebookHalf& cb, int32_t layer_begin, int32_t layer_count,
+                            hipStream_t s);
+
 size_t attend_workspace_bytes(const PoolGeom& g, int32_t n_agents, int32_t gqa,
                               int32_t layer_count, int32_t path);
 hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s);

@@ -20,7 +20,8 @@ POLYKV_MAX_ROWS = 64
 EXPORTED_SYMBOLS = (
     "polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k", "polykv_compress_v",
     "polykv_attend_workspace_bytes", "polykv_attend_path", "polykv_attend_shared", "polykv_attend_shared_path",
-    "polykv_attend_shared_lse", "polykv_attend_tail_merge", "polykv_strerror",
+    "polykv_attend_shared_lse", "polykv_attend_tail_merge", "polykv_dequant_k", "polykv_dequant_v",
+    "polykv_strerror",
 )
 
 
@@ -64,6 +65,9 @@ def lib():
         L.polykv_compress_k.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t), i32, i32, vp]
         L.polykv_compress_v.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t),
                                         ctypes.POINTER(polykv_codebook_t), i32, i32, vp]
+        L.polykv_dequant_k.argtypes = [vp, ctypes.POINTER(polykv_layout_t), vp, i32, i32, vp]
+        L.polykv_dequant_v.argtypes = [vp, ctypes.POINTER(polykv_layout_t), ctypes.POINTER(polykv_codebook_t),
+                                       vp, i32, i32, vp]
         L.polykv_attend_workspace_bytes.argtypes = [ctypes.POINTER(polykv_layout_t), i32, i32, i32]
         L.polykv_attend_workspace_bytes.restype = sz
         L.polykv_attend_path.argtypes = [ctypes.POINTER(polykv_layout_t), i32, i32]
@@ -149,6 +153,25 @@ def polykv_compress_v(v, pool, layout, cb=None, layer_begin=0, layer_count=None,
                                  ctypes.byref(layout), ctypes.byref(cb) if cb is not None else None,
                                  lb, lc, _stream_ptr(stream))
     _check(rc, "polykv_compress_v")
+
+
+def polykv_dequant_k(pool, layout, k, layer_begin=0, layer_count=None, stream=None):
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    if k.numel() != _kv_elems(layout, lc) or pool.numel() < layout.total_bytes:
+        raise ValueError("k or pool has the wrong size for the layout")
+    rc = lib().polykv_dequant_k(_dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
+                                _dev(k, torch.float16, "k"), lb, lc, _stream_ptr(stream))
+    _check(rc, "polykv_dequant_k")
+
+
+def polykv_dequant_v(pool, layout, v, cb=None, layer_begin=0, layer_count=None, stream=None):
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    if v.numel() != _kv_elems(layout, lc) or pool.numel() < layout.total_bytes:
+        raise ValueError("v or pool has the wrong size for the layout")
+    rc = lib().polykv_dequant_v(_dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
+                                ctypes.byref(cb) if cb is not None else None,
+                                _dev(v, torch.float16, "v"), lb, lc, _stream_ptr(stream))
+    _check(rc, "polykv_dequant_v")
 
 
 def polykv_attend_workspace_bytes(layout, n_agents, gqa, layer_count=None) -> int:

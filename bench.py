@@ -209,6 +209,13 @@ def main():
             e.append(ev())
         rec.append(e)
 
+    def dequant(i, which):
+        # pool copy i -> fp16 K or V (into the compress inputs, which are not needed again)
+        if which == "k":
+            pk.polykv_dequant_k(pools[i % n_pools], lay, k, stream=stream)
+        else:
+            pk.polykv_dequant_v(pools[i % n_pools], lay, v, stream=stream)
+
     def tail_merge(i):
         tk, tv = tails[i % len(tails)]
         pk.polykv_attend_tail_merge(lay, q[0], out, lse, tk, tv, tail_len, cfg.n_agents, cfg.gqa,
@@ -223,6 +230,9 @@ def main():
                                             cfg.softmax_scale, path, workspace=ws, stream=stream)
                 for i in range(2 * n_pools):
                     tail_merge(i)
+            for i in range(2 * n_pools):
+                dequant(i, "k")
+                dequant(i, "v")
             stream.synchronize()
             print("profile run done: %d steps x (2 compress + %d decode) launches"
                   % (n_pools + args.steps, D), flush=True)
@@ -266,6 +276,18 @@ def main():
                 if i >= n_pools:
                     tail_ev.append((e0, e1))
             stream.synchronize()
+
+        # Secondary figure: dequantisation of a pool back to fp16 K and V. It runs last,
+        # because it overwrites the compress inputs.
+        dq_ev = {"k": [], "v": []}
+        for which in ("k", "v"):
+            for i in range(n_pools + 12):
+                e0 = ev()
+                dequant(i, which)
+                e1 = ev()
+                if i >= n_pools:
+                    dq_ev[which].append((e0, e1))
+        stream.synchronize()
 
     step_ms = [r[0].elapsed_time(r[-1]) for r in rec]
     ck_ms = [r[0].elapsed_time(r[1]) for r in rec]
@@ -330,6 +352,18 @@ def main():
                                 "frac_hbm": tail_bytes / t_tail / 1e9 / HBM_PEAK_GBPS,
                                 "algorithmic_bytes_per_launch": tail_bytes,
                                 "traffic": _traffic("attend_tail", ["attend_tail.hip"], "%s_tail%d" % (workload, n_tail))}
+    t_dk = sum(a.elapsed_time(b) for a, b in dq_ev["k"]) / len(dq_ev["k"]) / 1e3
+    t_dv = sum(a.elapsed_time(b) for a, b in dq_ev["v"]) / len(dq_ev["v"]) / 1e3
+    # algorithmic bytes: the pool's K (or V) region read, fp16 K (or V) written
+    dk_bytes = cfg.kv_elems + cfg.kv_elems // 16 + fp16_bytes
+    dv_bytes = cfg.kv_elems * 3 // 8 + cfg.n_layers * cfg.n_kv_heads * cfg.n_tokens * 2 + fp16_bytes
+    result["dequant"] = {
+        "kernels": ["dequant_k", "dequant_v"], "us": {"k": t_dk * 1e6, "v": t_dv * 1e6},
+        "GBps": {"k": dk_bytes / t_dk / 1e9, "v": dv_bytes / t_dv / 1e9},
+        "frac_hbm": {"k": dk_bytes / t_dk / 1e9 / HBM_PEAK_GBPS, "v": dv_bytes / t_dv / 1e9 / HBM_PEAK_GBPS},
+        "algorithmic_bytes_per_launch": {"k": dk_bytes, "v": dv_bytes},
+        "traffic": {"k": _traffic("dequant_k", ["dequant.hip"], workload),
+                    "v": _traffic("dequant_v", ["dequant.hip"], workload)}}
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         n = args.cpu_sample_layers or cfg.n_layers

@@ -131,6 +131,33 @@ int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* lay
                       const polykv_codebook_t* cb, int32_t layer_begin, int32_t layer_count,
                       void* hip_stream);
 
+/*
+ * Pool -> fp16 keys. PolyKV, Abstract: the shared pool is handed to each agent as an
+ * ordinary per-layer KV cache; this reconstructs the keys of layers
+ * [layer_begin, layer_begin + layer_count):
+ *   k_fp16[l][h][t][i] = RNE16(code * s), s the stored fp16 scale of the 32-entry block.
+ * The product is exact in fp32, so the result is the correctly rounded fp16 of the exact
+ * reconstruction.
+ *  pool:   device, layout->total_bytes, 256-B aligned (read only).
+ *  k_fp16: device, contiguous [layer_count][n_kv_heads][n_tokens][head_dim] binary16,
+ *          16-B aligned (written).
+ * Errors: NULL, ALIGN, RANGE, LAYOUT, DEVICE, LAUNCH.
+ */
+int polykv_dequant_k(const void* pool, const polykv_layout_t* layout, void* k_fp16,
+                     int32_t layer_begin, int32_t layer_count, void* hip_stream);
+
+/*
+ * Pool -> fp16 values, as polykv_dequant_k: v_fp16[l][h][t] = RNE16((n16 / d) * H c[code])
+ * with n16 the stored norm, c the codebook centroids (cb: host pointer or NULL for the
+ * default; only the centroids are used) and H the +-1 Sylvester matrix (inverse of the
+ * compress rotation). The transform runs in fp32 before the one rounding to fp16, so an
+ * element can differ from the correctly rounded value by one fp16 ulp where the exact
+ * value lies within ~1e-6 relative of a rounding midpoint.
+ * Errors: NULL, ALIGN, RANGE, LAYOUT, CODEBOOK, DEVICE, LAUNCH.
+ */
+int polykv_dequant_v(const void* pool, const polykv_layout_t* layout, const polykv_codebook_t* cb,
+                     void* v_fp16, int32_t layer_begin, int32_t layer_count, void* hip_stream);
+
 /* Decode kernel choice for polykv_attend_shared_path. */
 #define POLYKV_PATH_AUTO 0   /* the library's choice for the row count                    */
 #define POLYKV_PATH_VALU 1   /* fp32 vector-ALU contraction                               */

@@ -82,3 +82,15 @@ def dequant_pool(pool: dict, centroids, n_tokens=None):
         codes = unpack_v_planes(pool["v_planes"], n_tokens)
     v_hat = tq_mse_decode(codes, pool["v_norms"], centroids)
     return k_hat, v_hat
+
+
+def dequant_fp16(pool: dict, centroids, n_tokens=None):
+    """The pool as fp16 K and V, the form an ordinary per-layer cache holds (PolyKV,
+    Abstract: the shared pool is handed to every agent as its KV cache).
+
+    Each element is the fp64 reconstruction of dequant_pool rounded once, to nearest
+    even, to binary16 (numpy's float64 -> float16 conversion rounds the double directly).
+    For keys the fp64 value code * s is exact, so this is the correctly rounded result.
+    """
+    k_hat, v_hat = dequant_pool(pool, centroids, n_tokens)
+    return k_hat.astype(np.float16), v_hat.astype(np.float16)

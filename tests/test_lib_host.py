@@ -172,6 +172,30 @@ def test_tail_merge_validation(L):
     assert call(cap=0, tk=None, tv=None) == 0   # nothing to merge: no device work at all
 
 
+def test_dequant_validation(L):
+    lay = _layout()
+    lb = ctypes.byref(lay)
+    for f in (L.polykv_dequant_k,):
+        assert f(None, lb, A16, 0, 2, None) == -1
+        assert f(A256, None, A16, 0, 2, None) == -1
+        assert f(A256, lb, None, 0, 2, None) == -1
+        assert f(ctypes.c_void_p(0x20010), lb, A16, 0, 2, None) == -3     # pool needs 256 B
+        assert f(A256, lb, ctypes.c_void_p(0x10008), 0, 2, None) == -3
+        assert f(A256, lb, A16, 1, 2, None) == -4
+        assert f(A256, lb, A16, 0, 0, None) == -4
+    assert L.polykv_dequant_v(None, lb, None, A16, 0, 2, None) == -1
+    assert L.polykv_dequant_v(A256, lb, None, None, 0, 2, None) == -1
+    assert L.polykv_dequant_v(ctypes.c_void_p(0x20010), lb, None, A16, 0, 2, None) == -3
+    assert L.polykv_dequant_v(A256, lb, None, A16, -1, 1, None) == -4
+    bad = _layout()
+    bad.total_bytes -= 1
+    assert L.polykv_dequant_k(A256, ctypes.byref(bad), A16, 0, 2, None) == -9
+    assert L.polykv_dequant_v(A256, ctypes.byref(bad), None, A16, 0, 2, None) == -9
+    cb = pk.polykv_codebook_default()
+    cb.centroid[6] += 1e-3       # no longer symmetric
+    assert L.polykv_dequant_v(A256, lb, ctypes.byref(cb), A16, 0, 2, None) == -8
+
+
 def test_strerror(L):
     for code in range(0, -11, -1):
         assert isinstance(pk.polykv_strerror(code), str) and pk.polykv_strerror(code)

@@ -78,3 +78,53 @@ def test_pages_memory_arithmetic(golden_dir):
     fp16_private = agents * fp16_kv_bytes(c3.n_layers, c3.n_kv_heads, c3.n_tokens, c3.head_dim)
     shared = analytic_pool_bytes(c3.n_layers, c3.n_kv_heads, c3.n_tokens, c3.head_dim)
     assert 1 - shared / fp16_private == pytest.approx(0.9758, abs=1e-4)
+
+
+def test_dequant_fp16_rounds_the_double_once():
+    """The fp16 step is one round-to-nearest-even of the fp64 value. Key values: with the
+    fp16 scale s = 1 + 2^-10, code 127 gives 127 + 127 * 2^-10, which lies between the
+    fp16 neighbours 127.0 and 127.125 (spacing 2^-4) and nearer the upper one. The
+    conversion itself is checked at a tie and just above it, where a float32 detour would
+    round twice and go the wrong way."""
+    from oracle import dequant_fp16
+    # one token-head, d = 32: code 127 * s with s = fp16(1 + 2^-10) is 127 + 127 * 2^-10,
+    # exact in fp64 and in fp32; fp16 spacing at 127 is 2^-4, so it rounds to 127.125
+    s = np.float16(1 + 2.0 ** -10)
+    codes = np.zeros((1, 1, 1, 32), dtype=np.int8)
+    codes[..., 0] = 127
+    codes[..., 1] = -127
+    codes[..., 2] = 1
+    pool = {"k_codes": codes, "k_scales": np.full((1, 1, 1, 1), s, dtype=np.float16),
+            "v_codes": np.full((1, 1, 1, 32), 3, dtype=np.uint8),
+            "v_norms": np.zeros((1, 1, 1), dtype=np.float16)}
+    c32, _ = codebook_fp32()
+    k16, v16 = dequant_fp16(pool, c32)
+    exact = 127 * (1 + 2.0 ** -10)
+    assert float(k16[0, 0, 0, 0]) == 127.125 and abs(exact - 127.125) < 2.0 ** -5
+    assert float(k16[0, 0, 0, 1]) == -127.125
+    assert float(k16[0, 0, 0, 2]) == float(s)
+    assert np.all(v16 == 0)
+    # the conversion itself: 1 + 2^-11 is a tie (to even: 1), 1 + 2^-11 + 2^-40 is above
+    # it (up), although a float32 detour would land on the tie first and go down
+    x = np.array([1 + 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -40, 1 + 3 * 2.0 ** -11])
+    assert list(x.astype(np.float16).astype(np.float64)) == [1.0, 1 + 2.0 ** -10, 1 + 2 * 2.0 ** -10]
+    assert np.float32(x[1]) == np.float32(x[0])  # the float32 detour loses the difference
+
+
+def test_dequant_fp16_matches_round_trip_bounds():
+    """fp16 reconstructions of a seeded pool: keys within s/2 of the input plus the fp16
+    rounding of the reconstruction (the q8_0 error bound), values equal elementwise to
+    the fp64 reconstruction rounded."""
+    from oracle import compress_pool, dequant_fp16, dequant_pool
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((1, 2, 40, 64)).astype(np.float16)
+    v = rng.standard_normal((1, 2, 40, 64)).astype(np.float16)
+    c32, b32 = codebook_fp32()
+    op = compress_pool(k, v, b32)
+    k16, v16 = dequant_fp16(op, c32)
+    kh, vh = dequant_pool(op, c32)
+    s = op["k_scales"].astype(np.float64).repeat(32, axis=-1)
+    err = np.abs(k16.astype(np.float64) - k.astype(np.float64))
+    assert np.all(err <= s / 2 + np.abs(kh) * 2.0 ** -11 + 1e-12)
+    np.testing.assert_array_equal(v16, vh.astype(np.float16))
+    assert k16.dtype == np.float16 and v16.dtype == np.float16
