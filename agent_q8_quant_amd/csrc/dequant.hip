@@ -12,6 +12,8 @@
 //          symmetric and H H = d I). The transform runs in fp32 (error far below one fp16
 //          ulp), then one rounding to fp16.
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -53,11 +55,12 @@ __global__ __launch_bounds__(256) void k_dequant_k(const uint8_t* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------------------
-// Values: one wave per item. For head_dim 128 and 256 an item is one 32-token group of a
-// tile and lane l holds token l % 32, coordinates (l / 32) * d/2 .. + d/2 - 1; for
-// head_dim 64 an item is two consecutive groups and lane l holds token l % 32 of group
-// l / 32, all 64 coordinates. Steps:
-// 1. the item's plane words (3 x d per group) are staged in LDS, one copy per wave;
+// Values. An item is one 32-token group of a tile for head_dim 128 and 256 (lane l holds
+// token l % 32, coordinates (l / 32) * d/2 .. + d/2 - 1) and two consecutive groups for
+// head_dim 64 (lane l holds token l % 32 of group l / 32, all 64 coordinates). Each wave
+// walks items with a grid stride and keeps the next item's plane words and norm in
+// registers while it works on the current one. Per item:
+// 1. the plane words (3 x d per group, as stored) go from registers to the wave's LDS area;
 // 2. lane l reads, per coordinate, the three words of its half and takes bit l % 32 of
 //    each: the code, whose centroid comes from an 8-entry LDS table;
 // 3. the FWHT runs in registers over the lane's coordinates, and for d >= 128 one last
@@ -68,10 +71,51 @@ template <int D>
 struct DqCfg {
     static constexpr int HALVES = D == 64 ? 1 : 2;   // lanes per token
     static constexpr int CPL = D / HALVES;           // coordinates per lane
-    static constexpr int GPW = D == 64 ? 2 : 1;      // groups per wave
+    static constexpr int GPW = D == 64 ? 2 : 1;      // groups per item
     static constexpr int WORDS = GPW * 3 * D;        // plane words per item
-    static constexpr int WAVE_LDS = WORDS * 4;
+    static constexpr int PIECES = WORDS / 4;         // 16-byte pieces per item
+    static constexpr int PPL = (PIECES + 63) / 64;   // pieces per lane
 };
+
+// Where item `item` lives, and its plane words and this lane's norm fetched into registers.
+template <int D>
+struct DqItem {
+    uint32_t tile_local;
+    int g0, n_grp, token;
+    bool valid;
+};
+
+template <int D>
+__device__ __forceinline__ DqItem<D> dq_item(uint32_t item, uint32_t items_per_tile, const PoolGeom& g, int lane) {
+    using C = DqCfg<D>;
+    DqItem<D> it;
+    it.tile_local = item / items_per_tile;
+    const uint32_t gi = item - it.tile_local * items_per_tile;
+    it.g0 = (int)gi * C::GPW;
+    it.n_grp = min(C::GPW, g.n_groups - it.g0);
+    const int half = lane >> 5, t = lane & 31;
+    it.token = 32 * (C::GPW == 2 ? it.g0 + half : it.g0) + t;
+    it.valid = it.token < g.n_tokens && (C::GPW == 1 || half < it.n_grp);
+    return it;
+}
+
+template <int D>
+__device__ __forceinline__ void dq_fetch(const DqItem<D>& it, const uint8_t* pool, const PoolGeom& g,
+                                         int32_t layer_begin, int lane, u4 (&pf)[DqCfg<D>::PPL],
+                                         uint32_t& norm_bits) {
+    using C = DqCfg<D>;
+    const size_t tile = (size_t)layer_begin * g.n_kv_heads + it.tile_local;
+    const u4* src = reinterpret_cast<const u4*>(pool + g.v_planes_off + tile * g.v_planes_stride +
+                                                (size_t)it.g0 * (3 * D * 4));
+    const int n_pieces = it.n_grp * 3 * D / 4;
+#pragma unroll
+    for (int i = 0; i < C::PPL; ++i) {
+        const int piece = lane + 64 * i;
+        if (piece < n_pieces) pf[i] = src[piece];
+    }
+    const uint16_t* norms = reinterpret_cast<const uint16_t*>(pool + g.v_norms_off + tile * g.v_norms_stride);
+    norm_bits = it.valid ? norms[it.token] : 0u;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ pool, PoolGeom g,
@@ -91,79 +135,91 @@ __global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ p
         ctab[tid] = tid >= 4 ? mag : -mag;
     }
     __syncthreads();  // the only workgroup barrier: waves without an item leave after it
-    const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4u + (uint32_t)w));
+    const uint32_t stride = gridDim.x * 4u;
+    uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4u + (uint32_t)w));
     if (item >= n_items) return;
-    const uint32_t tile_local = item / items_per_tile;
-    const uint32_t gi = item - tile_local * items_per_tile;
-    const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_local;
     const int T = g.n_tokens;
-    const int g0 = (int)gi * C::GPW;                       // first group of the item
-    const int n_grp = min(C::GPW, g.n_groups - g0);        // groups present (1 or GPW)
-
-    // 1. stage the plane words: [group][plane][d] as stored
-    const u4* src = reinterpret_cast<const u4*>(pool + g.v_planes_off + tile * g.v_planes_stride +
-                                                (size_t)g0 * (3 * D * 4));
-    u4* dst = reinterpret_cast<u4*>(&words[w][0]);
-    for (int i = lane; i < n_grp * 3 * D / 4; i += 64) dst[i] = src[i];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
     const int half = lane >> 5, t = lane & 31;
-    const int grp = C::GPW == 2 ? g0 + half : g0;
     const int coord0 = C::GPW == 2 ? 0 : half * CPL;
-    const int token = 32 * grp + t;
-    const bool valid = token < T && (C::GPW == 1 || half < n_grp);
     const uint32_t* wb = &words[w][(C::GPW == 2 ? half * 3 * D : 0) + coord0];
+    u4* stage = reinterpret_cast<u4*>(&words[w][0]);
 
-    // 2. codes -> centroids
-    float x[CPL];
+    u4 pf[C::PPL];
+    uint32_t norm_bits;
+    DqItem<D> it = dq_item<D>(item, items_per_tile, g, lane);
+    dq_fetch<D>(it, pool, g, layer_begin, lane, pf, norm_bits);
+    while (true) {
+        // 1. this item's words into LDS (the previous item's reads are complete: their
+        //    results were consumed before its stores)
+        {
+            const int n_pieces = it.n_grp * 3 * D / 4;
 #pragma unroll
-    for (int c = 0; c < CPL; c += 4) {
-        const u4 p0 = *reinterpret_cast<const u4*>(wb + c);
-        const u4 p1 = *reinterpret_cast<const u4*>(wb + D + c);
-        const u4 p2 = *reinterpret_cast<const u4*>(wb + 2 * D + c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t code = __builtin_amdgcn_ubfe(p0[e], t, 1) | (__builtin_amdgcn_ubfe(p1[e], t, 1) << 1) |
-                                  (__builtin_amdgcn_ubfe(p2[e], t, 1) << 2);
-            x[c + e] = ctab[code];
-        }
-    }
-    // 3. Sylvester FWHT over the lane's coordinates (pairs at distance h become (a+b, a-b))
-#pragma unroll
-    for (int h = 1; h < CPL; h <<= 1)
-#pragma unroll
-        for (int e = 0; e < CPL; ++e)
-            if (!(e & h)) {
-                const float a = x[e], b = x[e + h];
-                x[e] = a + b;
-                x[e + h] = a - b;
+            for (int i = 0; i < C::PPL; ++i) {
+                const int piece = lane + 64 * i;
+                if (piece < n_pieces) stage[piece] = pf[i];
             }
-    if constexpr (C::HALVES == 2) {
-        // coordinate bit log2(d/2): lower half (a) and upper half (b) of the same token
-        const float sgn = half ? -1.0f : 1.0f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-            const uint32_t u = __float_as_uint(x[e]);
-            const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-            // s[0]: the lower half's value in every lane, s[1]: the upper half's
-            x[e] = __builtin_fmaf(sgn, __uint_as_float(s[1]), __uint_as_float(s[0]));
         }
-    }
-    if (!valid) return;
-    // 4. scale by n / d and store
-    const __half* norms = reinterpret_cast<const __half*>(pool + g.v_norms_off + tile * g.v_norms_stride);
-    const float f = __half2float(norms[token]) * (1.0f / (float)D);
-    u4* o = reinterpret_cast<u4*>(out + ((size_t)tile_local * T + token) * D + coord0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const DqItem<D> cur = it;
+        const float f = __half2float(__ushort_as_half((unsigned short)norm_bits)) * (1.0f / (float)D);
+        const uint32_t next = item + stride;
+        if (next < n_items) {
+            it = dq_item<D>(next, items_per_tile, g, lane);
+            dq_fetch<D>(it, pool, g, layer_begin, lane, pf, norm_bits);  // in flight meanwhile
+        }
+
+        // 2. codes -> centroids
+        float x[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; c += 8) {
-        uint32_t q[4];
+        for (int c = 0; c < CPL; c += 4) {
+            const u4 p0 = *reinterpret_cast<const u4*>(wb + c);
+            const u4 p1 = *reinterpret_cast<const u4*>(wb + D + c);
+            const u4 p2 = *reinterpret_cast<const u4*>(wb + 2 * D + c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            q[e] = (uint32_t)__half_as_ushort(__float2half_rn(x[c + 2 * e] * f)) |
-                   ((uint32_t)__half_as_ushort(__float2half_rn(x[c + 2 * e + 1] * f)) << 16);
-        o[c / 8] = u4{q[0], q[1], q[2], q[3]};
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t code = __builtin_amdgcn_ubfe(p0[e], t, 1) | (__builtin_amdgcn_ubfe(p1[e], t, 1) << 1) |
+                                      (__builtin_amdgcn_ubfe(p2[e], t, 1) << 2);
+                x[c + e] = ctab[code];
+            }
+        }
+        // 3. Sylvester FWHT over the lane's coordinates (pairs at distance h become (a+b, a-b))
+#pragma unroll
+        for (int h = 1; h < CPL; h <<= 1)
+#pragma unroll
+            for (int e = 0; e < CPL; ++e)
+                if (!(e & h)) {
+                    const float a = x[e], b = x[e + h];
+                    x[e] = a + b;
+                    x[e + h] = a - b;
+                }
+        if constexpr (C::HALVES == 2) {
+            // coordinate bit log2(d/2): lower half (a) and upper half (b) of the same token
+            const float sgn = half ? -1.0f : 1.0f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const uint32_t u = __float_as_uint(x[e]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+                // sw[0]: the lower half's value in every lane, sw[1]: the upper half's
+                x[e] = __builtin_fmaf(sgn, __uint_as_float(sw[1]), __uint_as_float(sw[0]));
+            }
+        }
+        // 4. scale by n / d and store
+        if (cur.valid) {
+            u4* o = reinterpret_cast<u4*>(out + ((size_t)cur.tile_local * T + cur.token) * D + coord0);
+#pragma unroll
+            for (int c = 0; c < CPL; c += 8) {
+                uint32_t q[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    q[e] = (uint32_t)__half_as_ushort(__float2half_rn(x[c + 2 * e] * f)) |
+                           ((uint32_t)__half_as_ushort(__float2half_rn(x[c + 2 * e + 1] * f)) << 16);
+                o[c / 8] = u4{q[0], q[1], q[2], q[3]};
+            }
+        }
+        if (next >= n_items) break;
+        item = next;
     }
 }
 
@@ -185,7 +241,8 @@ hipError_t launch_dequant_v(const uint8_t* pool, void* v_fp16, const PoolGeom& g
     const uint32_t gpw = g.head_dim == 64 ? 2u : 1u;
     const uint32_t items_per_tile = ((uint32_t)g.n_groups + gpw - 1) / gpw;
     const uint64_t items = (uint64_t)layer_count * g.n_kv_heads * items_per_tile;
-    const uint32_t blocks = (uint32_t)((items + 3) / 4);
+    // waves walk the items with a grid stride; 2048 workgroups (8 per CU) cover the chip
+    const uint32_t blocks = (uint32_t)std::min<uint64_t>((items + 3) / 4, 2048);
     __half* out = (__half*)v_fp16;
     switch (g.head_dim) {
         case 64: hipLaunchKernelGGL(k_dequant_v<64>, dim3(blocks), dim3(256), 0, s, pool, g, cb, layer_begin, items_per_tile, (uint32_t)items, out); break;
