@@ -499,7 +499,14 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
                 // probabilities (scaled by 2^-slack) in fp16; row sums of the weighted fp16
                 // probabilities; P.V operand p * n * weight
                 const h8 wt = {m_lo[0], m_lo[1], m_lo[2], m_lo[3], m_hi[0], m_hi[1], m_hi[2], m_hi[3]};
-                const h8 nn = h8{n_lo[0], n_lo[1], n_lo[2], n_lo[3], n_hi[0], n_hi[1], n_hi[2], n_hi[3]} * wt;
+                h8 nv = h8{n_lo[0], n_lo[1], n_lo[2], n_lo[3], n_hi[0], n_hi[1], n_hi[2], n_hi[3]};
+                if (t0 + CHUNK > T) {
+                    // the tile's last chunk: norm slots past T may hold any bits (padding, or
+                    // tokens not written yet), so they are replaced by 0, not multiplied by it
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) nv[e] = wt[e] != (_Float16)0.0f ? nv[e] : (_Float16)0.0f;
+                }
+                const h8 nn = nv * wt;
                 h8* pb = pbuf + (k & 1) * NRB * 64;
 #pragma unroll
                 for (int rb = 0; rb < SRB; ++rb) {

@@ -17,7 +17,8 @@ namespace {
 // ---------------------------------------------------------------------------------------
 // Keys. One thread owns 8 consecutive entries (one 16-B load); the 4 threads of a quad
 // own one 32-entry block and combine their |x| maxima through two lane exchanges.
-// Grid: x over 8-entry vectors of a tile, y over the tiles of the layer range.
+// Grid: x over the 8-entry vectors of a tile's token range, y over the tiles of the layer
+// range. The input holds that token range only: [layer_count][H][n_tok][d].
 //
 // Arithmetic, equal to the definition (IEEE amax / 127, round-half-even of x / s):
 // - m / 127 for an fp16 m lies at least 1/254 of an fp16 ulp from every fp16 rounding
@@ -30,7 +31,8 @@ namespace {
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_compress_k(const uint4* __restrict__ k,
                                                     uint8_t* __restrict__ pool, PoolGeom g,
-                                                    int32_t layer_begin, uint32_t vec_per_tile) {
+                                                    int32_t layer_begin, uint32_t vec_per_tile,
+                                                    uint32_t tok0) {
     const uint32_t tile_local = blockIdx.y;
     const uint32_t v = blockIdx.x * 256u + threadIdx.x;
     // vec_per_tile is a multiple of 4, so a quad is either wholly active or wholly idle
@@ -64,12 +66,36 @@ __global__ __launch_bounds__(256) void k_compress_k(const uint4* __restrict__ k,
     }
     if (!active) return;
     const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_local;
+    const size_t v0 = (size_t)tok0 * (g.head_dim / 8);  // first 8-entry vector of the range
     uint2* codes = reinterpret_cast<uint2*>(pool + g.k_codes_off + tile * g.k_codes_stride);
-    codes[v] = make_uint2(packed[0], packed[1]);
+    codes[v0 + v] = make_uint2(packed[0], packed[1]);
     if ((threadIdx.x & 3) == 0) {
         __half* scales = reinterpret_cast<__half*>(pool + g.k_scales_off + tile * g.k_scales_stride);
-        scales[v >> 2] = s16;
+        scales[(v0 + v) >> 2] = s16;
     }
+}
+
+// Token range [tok0, tok0 + n_tok) of every tile (the whole tile for a one-shot compress,
+// one prefill chunk for an append) and the 32-token groups it touches. The input holds the
+// range only, [layer_count][H][n_tok][d]. A group the range covers only in part keeps the
+// plane bits of its other tokens below the tile's length: the new words are
+// (old & keep) | new bits. Bits of tokens at or past the tile's length are always 0.
+struct TokRange {
+    uint32_t tok0, n_tok, g_first, n_grp;
+};
+
+__device__ __forceinline__ uint32_t keep_mask(const TokRange& r, uint32_t grp, uint32_t T) {
+    uint32_t keep = 0u;
+    const uint32_t t_base = grp * 32u;
+    // tokens of the group below the range, and those past it but below T
+    if (r.tok0 > t_base) keep |= (r.tok0 - t_base >= 32u) ? 0xFFFFFFFFu : ((1u << (r.tok0 - t_base)) - 1u);
+    const uint32_t end = r.tok0 + r.n_tok, lim = min(T, t_base + 32u);
+    if (lim > end) {
+        const uint32_t lo = max(end, t_base) - t_base, hi = lim - t_base;  // [lo, hi)
+        const uint32_t upto_hi = hi >= 32u ? 0xFFFFFFFFu : ((1u << hi) - 1u);
+        keep |= upto_hi & ~((1u << lo) - 1u);
+    }
+    return keep;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -82,22 +108,21 @@ template <int D>
 __global__ __launch_bounds__(256) void k_compress_v(const __half* __restrict__ v,
                                                     uint8_t* __restrict__ pool, PoolGeom g,
                                                     CodebookHalf cb, int32_t layer_begin,
-                                                    uint32_t n_items) {
+                                                    uint32_t n_items, TokRange rg) {
     constexpr int NW = D / 64;  // coordinates per lane in the word buffer
     const int lane = threadIdx.x & 63;
     const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
-    const uint32_t G = (uint32_t)g.n_groups;
     const uint32_t T = (uint32_t)g.n_tokens;
 
     const uint32_t item = wave * 2u + (uint32_t)(lane >> 5);
-    const uint32_t tile_local = item / G;
-    const uint32_t grp = item - tile_local * G;
+    const uint32_t tile_local = item / rg.n_grp;
+    const uint32_t grp = rg.g_first + (item - tile_local * rg.n_grp);
     const uint32_t token = grp * 32u + (uint32_t)(lane & 31);
-    const bool valid = item < n_items && token < T;
+    const bool valid = item < n_items && token >= rg.tok0 && token < rg.tok0 + rg.n_tok;
 
     float x[D];
     if (valid) {
-        const uint4* src = reinterpret_cast<const uint4*>(v + ((size_t)tile_local * T + token) * D);
+        const uint4* src = reinterpret_cast<const uint4*>(v + ((size_t)tile_local * rg.n_tok + (token - rg.tok0)) * D);
 #pragma unroll
         for (int c = 0; c < D / 8; ++c) {
             uint4 r = src[c];
@@ -170,8 +195,9 @@ __global__ __launch_bounds__(256) void k_compress_v(const __half* __restrict__ v
     for (int half = 0; half < 2; ++half) {
         const uint32_t it = wave * 2u + (uint32_t)half;
         if (it >= n_items) continue;
-        const uint32_t tl = it / G;
-        const uint32_t gr = it - tl * G;
+        const uint32_t tl = it / rg.n_grp;
+        const uint32_t gr = rg.g_first + (it - tl * rg.n_grp);
+        const uint32_t keep = keep_mask(rg, gr, T);
         uint32_t* words = reinterpret_cast<uint32_t*>(pool + g.v_planes_off +
                                                       (tile_base + tl) * g.v_planes_stride) +
                           (size_t)gr * 3 * D;
@@ -179,7 +205,9 @@ __global__ __launch_bounds__(256) void k_compress_v(const __half* __restrict__ v
         for (int p = 0; p < 3; ++p)
 #pragma unroll
             for (int c = 0; c < NW; ++c) {
-                words[p * D + c * 64 + lane] = half ? whi[p][c] : wlo[p][c];
+                const uint32_t nw = half ? whi[p][c] : wlo[p][c];
+                uint32_t* dst = &words[p * D + c * 64 + lane];
+                *dst = keep ? ((*dst & keep) | nw) : nw;
             }
     }
     if (valid) {
@@ -217,7 +245,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_compress_v_mfma(const __half* __restrict__ v,
                                                          uint8_t* __restrict__ pool, PoolGeom g,
                                                          CodebookHalf cb, int32_t layer_begin,
-                                                         uint32_t n_items) {
+                                                         uint32_t n_items, TokRange rg) {
     constexpr int KK = D / 16;        // k steps of the rotation
     constexpr int MB = D / 32;        // 32-dim output blocks
     constexpr int WPL = 3 * D / 64;   // plane words per lane of the store
@@ -226,12 +254,11 @@ __global__ __launch_bounds__(256) void k_compress_v_mfma(const __half* __restric
     // wave-uniform (and known to be so: scalar registers and branches)
     const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256u + threadIdx.x) >> 6));
     if (item >= n_items) return;  // whole waves only
-    const uint32_t G = (uint32_t)g.n_groups;
     const uint32_t T = (uint32_t)g.n_tokens;
-    const uint32_t tile_local = item / G;
-    const uint32_t grp = item - tile_local * G;
+    const uint32_t tile_local = item / rg.n_grp;
+    const uint32_t grp = rg.g_first + (item - tile_local * rg.n_grp);
     const uint32_t token = grp * 32u + (uint32_t)l32;
-    const bool valid = token < T;
+    const bool valid = token >= rg.tok0 && token < rg.tok0 + rg.n_tok;
 
     // Sylvester fragments for even and odd k steps
     h8 F[2];
@@ -246,7 +273,7 @@ __global__ __launch_bounds__(256) void k_compress_v_mfma(const __half* __restric
     // B operand: token l % 32, dims 16 kk + 8 (l / 32) .. +7 (16 contiguous bytes)
     h8 vb[KK];
     {
-        const h8* src = reinterpret_cast<const h8*>(v + ((size_t)tile_local * T + (valid ? token : 0u)) * D + 8 * hl);
+        const h8* src = reinterpret_cast<const h8*>(v + ((size_t)tile_local * rg.n_tok + (valid ? token - rg.tok0 : 0u)) * D + 8 * hl);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) vb[kk] = valid ? src[2 * kk] : h8{};
     }
@@ -267,8 +294,8 @@ __global__ __launch_bounds__(256) void k_compress_v_mfma(const __half* __restric
     }
     const float n = sqrtf(ss);
     // y / n > b  <=>  y > b n for n > 0; n = 0 gives y = 0 and infinite thresholds (every
-    // code 3). Tokens past T have y = 0 and get thresholds -1: then every plane bit below
-    // comes out 0, as the layout requires.
+    // code 3). Tokens outside the range have y = 0 and get thresholds -1: then every plane
+    // bit below comes out 0 (bits past T must be 0; others are merged back by keep_mask).
     const float inv_t = valid ? (n > 0.0f ? 1.0f : INFINITY) : -1.0f;
     const float t4 = n > 0.0f ? cb.boundary_pos[0] * n : inv_t;
     const float t5 = n > 0.0f ? cb.boundary_pos[1] * n : inv_t;
@@ -317,8 +344,14 @@ __global__ __launch_bounds__(256) void k_compress_v_mfma(const __half* __restric
     const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_local;
     uint32_t* words = reinterpret_cast<uint32_t*>(pool + g.v_planes_off + tile * g.v_planes_stride) +
                       (size_t)grp * 3 * D;
+    const uint32_t keep = keep_mask(rg, grp, T);  // wave-uniform
+    if (keep) {
 #pragma unroll
-    for (int r = 0; r < WPL; ++r) words[64 * r + lane] = wv[r];
+        for (int r = 0; r < WPL; ++r) words[64 * r + lane] = (words[64 * r + lane] & keep) | wv[r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < WPL; ++r) words[64 * r + lane] = wv[r];
+    }
     if (hl == 0 && valid) {
         __half* norms = reinterpret_cast<__half*>(pool + g.v_norms_off + tile * g.v_norms_stride);
         norms[token] = __float2half_rn(n);
@@ -327,31 +360,48 @@ __global__ __launch_bounds__(256) void k_compress_v_mfma(const __half* __restric
 
 }  // namespace
 
-hipError_t launch_compress_k(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
-                             int32_t layer_begin, int32_t layer_count, hipStream_t s) {
-    const uint32_t vec_per_tile = (uint32_t)((uint64_t)g.n_tokens * g.head_dim / 8);
+hipError_t launch_compress_k_range(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
+                                   int32_t tok0, int32_t n_tok, int32_t layer_begin,
+                                   int32_t layer_count, hipStream_t s) {
+    const uint32_t vec_per_tile = (uint32_t)((uint64_t)n_tok * g.head_dim / 8);
     const uint32_t tiles = (uint32_t)layer_count * (uint32_t)g.n_kv_heads;
     dim3 grid((vec_per_tile + 255) / 256, tiles);
     hipLaunchKernelGGL(k_compress_k, grid, dim3(256), 0, s, (const uint4*)k_fp16, pool, g,
-                       layer_begin, vec_per_tile);
+                       layer_begin, vec_per_tile, (uint32_t)tok0);
     return hipGetLastError();
 }
 
-hipError_t launch_compress_v(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
-                             const CodebookHalf& cb, int32_t layer_begin, int32_t layer_count,
-                             hipStream_t s) {
-    const uint64_t items = (uint64_t)layer_count * g.n_kv_heads * g.n_groups;
+hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
+                                   const CodebookHalf& cb, int32_t tok0, int32_t n_tok,
+                                   int32_t layer_begin, int32_t layer_count, hipStream_t s) {
+    TokRange rg;
+    rg.tok0 = (uint32_t)tok0;
+    rg.n_tok = (uint32_t)n_tok;
+    rg.g_first = (uint32_t)tok0 / 32u;
+    rg.n_grp = (uint32_t)(tok0 + n_tok - 1) / 32u - rg.g_first + 1u;
+    const uint64_t items = (uint64_t)layer_count * g.n_kv_heads * rg.n_grp;
     const uint64_t waves = (items + 1) / 2;
     const uint32_t blocks = (uint32_t)((waves + 3) / 4);
     const __half* v = (const __half*)v_fp16;
     const uint32_t mblocks = (uint32_t)((items + 3) / 4);  // one wave per 32-token group
     switch (g.head_dim) {
-        case 64: hipLaunchKernelGGL(k_compress_v_mfma<64>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items); break;
-        case 128: hipLaunchKernelGGL(k_compress_v_mfma<128>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items); break;
-        case 256: hipLaunchKernelGGL(k_compress_v<256>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items); break;
+        case 64: hipLaunchKernelGGL(k_compress_v_mfma<64>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+        case 128: hipLaunchKernelGGL(k_compress_v_mfma<128>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+        case 256: hipLaunchKernelGGL(k_compress_v<256>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_compress_k(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
+                             int32_t layer_begin, int32_t layer_count, hipStream_t s) {
+    return launch_compress_k_range(k_fp16, pool, g, 0, g.n_tokens, layer_begin, layer_count, s);
+}
+
+hipError_t launch_compress_v(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
+                             const CodebookHalf& cb, int32_t layer_begin, int32_t layer_count,
+                             hipStream_t s) {
+    return launch_compress_v_range(v_fp16, pool, g, cb, 0, g.n_tokens, layer_begin, layer_count, s);
 }
 
 }  // namespace polykv

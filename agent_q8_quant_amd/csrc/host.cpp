@@ -238,6 +238,44 @@ int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* lay
                                                (hipStream_t)hip_stream));
 }
 
+static int check_tokens(const polykv_layout_t& l, int32_t token_begin, int32_t n_new) {
+    if (token_begin < 0 || n_new < 1 || (int64_t)token_begin + n_new > l.shape.n_tokens)
+        return POLYKV_ERR_RANGE;
+    return POLYKV_OK;
+}
+
+int polykv_append_k(const void* k_fp16, void* pool, const polykv_layout_t* layout,
+                    int32_t token_begin, int32_t n_new, int32_t layer_begin, int32_t layer_count,
+                    void* hip_stream) {
+    if (!k_fp16 || !pool || !layout) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (!aligned(pool, 256) || !aligned(k_fp16, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
+    if ((rc = check_tokens(*layout, token_begin, n_new))) return rc;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_compress_k_range(k_fp16, (uint8_t*)pool, polykv::make_geom(*layout),
+                                                     token_begin, n_new, layer_begin, layer_count,
+                                                     (hipStream_t)hip_stream));
+}
+
+int polykv_append_v(const void* v_fp16, void* pool, const polykv_layout_t* layout,
+                    const polykv_codebook_t* cb, int32_t token_begin, int32_t n_new,
+                    int32_t layer_begin, int32_t layer_count, void* hip_stream) {
+    if (!v_fp16 || !pool || !layout) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (!aligned(pool, 256) || !aligned(v_fp16, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
+    if ((rc = check_tokens(*layout, token_begin, n_new))) return rc;
+    const polykv_codebook_t& book = cb ? *cb : default_codebook();
+    if (!codebook_ok(book)) return POLYKV_ERR_CODEBOOK;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_compress_v_range(v_fp16, (uint8_t*)pool, polykv::make_geom(*layout),
+                                                     half_of(book), token_begin, n_new, layer_begin,
+                                                     layer_count, (hipStream_t)hip_stream));
+}
+
 int polykv_dequant_k(const void* pool, const polykv_layout_t* layout, void* k_fp16,
                      int32_t layer_begin, int32_t layer_count, void* hip_stream) {
     if (!pool || !layout || !k_fp16) return POLYKV_ERR_NULL;
@@ -292,11 +330,11 @@ size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_ag
                                           resolve_path(g, rows, POLYKV_PATH_AUTO));
 }
 
-int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
-                             const polykv_codebook_t* cb, const float* q, float* out,
-                             float* lse, int32_t n_agents, int32_t gqa, float softmax_scale,
-                             int32_t layer_begin, int32_t layer_count, void* workspace,
-                             size_t workspace_bytes, void* hip_stream, int32_t path) {
+static int attend_impl(const void* pool, const polykv_layout_t* layout,
+                       const polykv_codebook_t* cb, const float* q, float* out, float* lse,
+                       int32_t n_valid, int32_t n_agents, int32_t gqa, float softmax_scale,
+                       int32_t layer_begin, int32_t layer_count, void* workspace,
+                       size_t workspace_bytes, void* hip_stream, int32_t path) {
     if (!pool || !layout || !q || !out) return POLYKV_ERR_NULL;
     if (lse && !aligned(lse, 4)) return POLYKV_ERR_ALIGN;
     int rc = check_layout(layout);
@@ -309,7 +347,10 @@ int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
     if (path < POLYKV_PATH_AUTO || path > POLYKV_PATH_MFMA) return POLYKV_ERR_ARG;
     const polykv_codebook_t& book = cb ? *cb : default_codebook();
     if (!codebook_ok(book)) return POLYKV_ERR_CODEBOOK;
+    if (n_valid < 1 || n_valid > layout->shape.n_tokens) return POLYKV_ERR_RANGE;
     polykv::PoolGeom g = polykv::make_geom(*layout);
+    g.n_tokens = n_valid;               // attend over tokens [0, n_valid) of every tile
+    g.n_groups = (n_valid + 31) / 32;   // (strides and offsets stay those of the layout)
     const int rows = n_agents * gqa;
     path = resolve_path(g, rows, path);
     if (path == POLYKV_PATH_MFMA && !polykv::attend_mfma_supported(g, rows)) return POLYKV_ERR_SHAPE;
@@ -334,6 +375,26 @@ int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
     hipStream_t s = (hipStream_t)hip_stream;
     return launch_rc(path == POLYKV_PATH_MFMA ? polykv::launch_attend_mfma(a, s)
                                               : polykv::launch_attend_valu(a, s));
+}
+
+int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
+                             const polykv_codebook_t* cb, const float* q, float* out,
+                             float* lse, int32_t n_agents, int32_t gqa, float softmax_scale,
+                             int32_t layer_begin, int32_t layer_count, void* workspace,
+                             size_t workspace_bytes, void* hip_stream, int32_t path) {
+    return attend_impl(pool, layout, cb, q, out, lse, layout ? layout->shape.n_tokens : 1,
+                       n_agents, gqa, softmax_scale, layer_begin, layer_count, workspace,
+                       workspace_bytes, hip_stream, path);
+}
+
+int polykv_attend_shared_prefix(const void* pool, const polykv_layout_t* layout,
+                                const polykv_codebook_t* cb, const float* q, float* out,
+                                float* lse, int32_t n_valid, int32_t n_agents, int32_t gqa,
+                                float softmax_scale, int32_t layer_begin, int32_t layer_count,
+                                void* workspace, size_t workspace_bytes, void* hip_stream,
+                                int32_t path) {
+    return attend_impl(pool, layout, cb, q, out, lse, n_valid, n_agents, gqa, softmax_scale,
+                       layer_begin, layer_count, workspace, workspace_bytes, hip_stream, path);
 }
 
 int polykv_attend_shared_path(const void* pool, const polykv_layout_t* layout,

@@ -48,6 +48,14 @@ struct CodebookHalf {
 // launch. Arguments are already validated.
 hipError_t launch_compress_k(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
                              int32_t layer_begin, int32_t layer_count, hipStream_t s);
+// The same over tokens [tok0, tok0 + n_tok) of every tile, from an input that holds that
+// range only ([layer_count][H][n_tok][d]); plane bits of other tokens are kept.
+hipError_t launch_compress_k_range(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
+                                   int32_t tok0, int32_t n_tok, int32_t layer_begin,
+                                   int32_t layer_count, hipStream_t s);
+hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
+                                   const CodebookHalf& cb, int32_t tok0, int32_t n_tok,
+                                   int32_t layer_begin, int32_t layer_count, hipStream_t s);
 hipError_t launch_compress_v(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
                              const CodebookHalf& cb, int32_t layer_begin,
                              int32_t layer_count, hipStream_t s);

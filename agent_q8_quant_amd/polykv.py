@@ -20,8 +20,8 @@ POLYKV_MAX_ROWS = 64
 EXPORTED_SYMBOLS = (
     "polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k", "polykv_compress_v",
     "polykv_attend_workspace_bytes", "polykv_attend_path", "polykv_attend_shared", "polykv_attend_shared_path",
-    "polykv_attend_shared_lse", "polykv_attend_tail_merge", "polykv_dequant_k", "polykv_dequant_v",
-    "polykv_strerror",
+    "polykv_attend_shared_lse", "polykv_attend_shared_prefix", "polykv_attend_tail_merge",
+    "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v", "polykv_strerror",
 )
 
 
@@ -77,13 +77,18 @@ def lib():
         L.polykv_attend_shared.argtypes = att
         L.polykv_attend_shared_path.argtypes = att + [i32]
         L.polykv_attend_shared_lse.argtypes = att[:5] + [vp] + att[5:] + [i32]
+        L.polykv_attend_shared_prefix.argtypes = att[:5] + [vp, i32] + att[5:] + [i32]
+        L.polykv_append_k.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t), i32, i32, i32, i32, vp]
+        L.polykv_append_v.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t), ctypes.POINTER(polykv_codebook_t),
+                                      i32, i32, i32, i32, vp]
         L.polykv_attend_tail_merge.argtypes = [ctypes.POINTER(polykv_layout_t), vp, vp, vp, vp, vp, vp,
                                                i32, i32, i32, ctypes.c_float, i32, vp]
         L.polykv_strerror.argtypes = [ctypes.c_int]
         L.polykv_strerror.restype = ctypes.c_char_p
         for name in ("polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k",
                      "polykv_compress_v", "polykv_attend_shared", "polykv_attend_shared_path",
-                     "polykv_attend_shared_lse", "polykv_attend_tail_merge"):
+                     "polykv_attend_shared_lse", "polykv_attend_shared_prefix", "polykv_attend_tail_merge",
+                     "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -155,6 +160,38 @@ def polykv_compress_v(v, pool, layout, cb=None, layer_begin=0, layer_count=None,
     _check(rc, "polykv_compress_v")
 
 
+def _append_size(layout, t, n_new, lc, name):
+    s = layout.shape
+    if t.numel() != lc * s.n_kv_heads * int(n_new) * s.head_dim:
+        raise ValueError("%s has the wrong size for the chunk" % name)
+
+
+def polykv_append_k(k, pool, layout, token_begin, n_new=None, layer_begin=0, layer_count=None, stream=None):
+    """Compress the chunk k [layer_count][H][n_new][d] into tokens [token_begin, +n_new)."""
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    n_new = int(k.shape[-2]) if n_new is None else int(n_new)
+    _append_size(layout, k, n_new, lc, "k")
+    if pool.numel() < layout.total_bytes:
+        raise ValueError("pool has the wrong size for the layout")
+    rc = lib().polykv_append_k(_dev(k, torch.float16, "k"), _dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
+                               int(token_begin), n_new, lb, lc, _stream_ptr(stream))
+    _check(rc, "polykv_append_k")
+
+
+def polykv_append_v(v, pool, layout, token_begin, n_new=None, cb=None, layer_begin=0, layer_count=None,
+                    stream=None):
+    """Compress the chunk v [layer_count][H][n_new][d] into tokens [token_begin, +n_new)."""
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    n_new = int(v.shape[-2]) if n_new is None else int(n_new)
+    _append_size(layout, v, n_new, lc, "v")
+    if pool.numel() < layout.total_bytes:
+        raise ValueError("pool has the wrong size for the layout")
+    rc = lib().polykv_append_v(_dev(v, torch.float16, "v"), _dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
+                               ctypes.byref(cb) if cb is not None else None, int(token_begin), n_new, lb, lc,
+                               _stream_ptr(stream))
+    _check(rc, "polykv_append_v")
+
+
 def polykv_dequant_k(pool, layout, k, layer_begin=0, layer_count=None, stream=None):
     lb, lc = _layers(layout, layer_begin, layer_count)
     if k.numel() != _kv_elems(layout, lc) or pool.numel() < layout.total_bytes:
@@ -185,9 +222,7 @@ def polykv_attend_path(layout, n_agents, gqa) -> int:
     return rc
 
 
-def polykv_attend_shared_lse(pool, layout, q, out, lse, n_agents, gqa, softmax_scale,
-                             path=POLYKV_PATH_AUTO, layer_begin=0, layer_count=None, cb=None,
-                             workspace=None, stream=None):
+def _attend_ptrs(pool, layout, q, out, lse, n_agents, gqa, layer_begin, layer_count, cb, workspace):
     lb, lc = _layers(layout, layer_begin, layer_count)
     s = layout.shape
     n = lc * n_agents * s.n_kv_heads * gqa * s.head_dim
@@ -201,13 +236,29 @@ def polykv_attend_shared_lse(pool, layout, q, out, lse, n_agents, gqa, softmax_s
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, torch.uint8, "workspace"), workspace.numel()
-    rc = lib().polykv_attend_shared_lse(
-        _dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
-        ctypes.byref(cb) if cb is not None else None,
-        _dev(q, torch.float32, "q"), _dev(out, torch.float32, "out"), lse_ptr,
-        int(n_agents), int(gqa), float(softmax_scale), lb, lc, ws_ptr, ws_bytes,
-        _stream_ptr(stream), int(path))
+    return (_dev(pool, torch.uint8, "pool"), ctypes.byref(layout), ctypes.byref(cb) if cb is not None else None,
+            _dev(q, torch.float32, "q"), _dev(out, torch.float32, "out"), lse_ptr), lb, lc, ws_ptr, ws_bytes
+
+
+def polykv_attend_shared_lse(pool, layout, q, out, lse, n_agents, gqa, softmax_scale,
+                             path=POLYKV_PATH_AUTO, layer_begin=0, layer_count=None, cb=None,
+                             workspace=None, stream=None):
+    head, lb, lc, ws_ptr, ws_bytes = _attend_ptrs(pool, layout, q, out, lse, n_agents, gqa,
+                                                  layer_begin, layer_count, cb, workspace)
+    rc = lib().polykv_attend_shared_lse(*head, int(n_agents), int(gqa), float(softmax_scale), lb, lc,
+                                        ws_ptr, ws_bytes, _stream_ptr(stream), int(path))
     _check(rc, "polykv_attend_shared_lse")
+
+
+def polykv_attend_shared_prefix(pool, layout, q, out, lse, n_valid, n_agents, gqa, softmax_scale,
+                                path=POLYKV_PATH_AUTO, layer_begin=0, layer_count=None, cb=None,
+                                workspace=None, stream=None):
+    head, lb, lc, ws_ptr, ws_bytes = _attend_ptrs(pool, layout, q, out, lse, n_agents, gqa,
+                                                  layer_begin, layer_count, cb, workspace)
+    rc = lib().polykv_attend_shared_prefix(*head, int(n_valid), int(n_agents), int(gqa),
+                                           float(softmax_scale), lb, lc, ws_ptr, ws_bytes,
+                                           _stream_ptr(stream), int(path))
+    _check(rc, "polykv_attend_shared_prefix")
 
 
 def polykv_attend_shared_path(pool, layout, q, out, n_agents, gqa, softmax_scale, path,

@@ -132,6 +132,30 @@ int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* lay
                       void* hip_stream);
 
 /*
+ * Chunked (append) compression. PolyKV, Abstract: the pool is written a single time; when
+ * the shared context arrives in prefill chunks, each chunk is written once, into its own
+ * token range. These compress tokens [token_begin, token_begin + n_new) of every tile of
+ * layers [layer_begin, layer_begin + layer_count) exactly as polykv_compress_k/v would
+ * compress them within the whole context (every step is per token), so appending the
+ * chunks of a context in any order gives the same pool bytes as one compress of it.
+ *  k_fp16 / v_fp16: device binary16, contiguous [layer_count][n_kv_heads][n_new][head_dim]
+ *          (the chunk only), 16-B aligned.
+ *  pool:   device, layout->total_bytes, 256-B aligned; layout->shape.n_tokens is the
+ *          capacity. Only the chunk's codes, scales, norms and plane bits are written: the
+ *          plane words of a 32-token group the chunk covers in part are read, and the bits
+ *          of the group's other tokens below the capacity are kept.
+ *  cb (values): host pointer or NULL for polykv_codebook_default.
+ * Calls whose chunks share a 32-token group must not run concurrently (stream order).
+ * Errors: NULL, ALIGN, RANGE (token or layer range), LAYOUT, CODEBOOK, DEVICE, LAUNCH.
+ */
+int polykv_append_k(const void* k_fp16, void* pool, const polykv_layout_t* layout,
+                    int32_t token_begin, int32_t n_new, int32_t layer_begin, int32_t layer_count,
+                    void* hip_stream);
+int polykv_append_v(const void* v_fp16, void* pool, const polykv_layout_t* layout,
+                    const polykv_codebook_t* cb, int32_t token_begin, int32_t n_new,
+                    int32_t layer_begin, int32_t layer_count, void* hip_stream);
+
+/*
  * Pool -> fp16 keys. PolyKV, Abstract: the shared pool is handed to each agent as an
  * ordinary per-layer KV cache; this reconstructs the keys of layers
  * [layer_begin, layer_begin + layer_count):
@@ -211,6 +235,19 @@ int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
                              int32_t layer_begin, int32_t layer_count,
                              void* workspace, size_t workspace_bytes, void* hip_stream,
                              int32_t path);
+
+/*
+ * As polykv_attend_shared_lse over tokens [0, n_valid) of every tile only, for a pool that
+ * is filled by polykv_append_k/v up to n_valid tokens (1 <= n_valid <= n_tokens). Tokens
+ * at or past n_valid are never used, whatever their bytes hold.
+ * Errors: as polykv_attend_shared_path; RANGE also for n_valid outside [1, n_tokens].
+ */
+int polykv_attend_shared_prefix(const void* pool, const polykv_layout_t* layout,
+                                const polykv_codebook_t* cb, const float* q, float* out,
+                                float* lse, int32_t n_valid, int32_t n_agents, int32_t gqa,
+                                float softmax_scale, int32_t layer_begin, int32_t layer_count,
+                                void* workspace, size_t workspace_bytes, void* hip_stream,
+                                int32_t path);
 
 /*
  * Private tails. PolyKV, Abstract: the one compressed pool is handed to N separate agent

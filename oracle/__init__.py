@@ -31,6 +31,6 @@ from .hadamard import fwht, hadamard_matrix  # noqa: F401
 from .q8_0 import q8_0_encode, q8_0_decode  # noqa: F401
 from .turboquant import tq_mse_encode, tq_mse_decode, rotated_coordinates  # noqa: F401
 from .pool import (pack_v_planes, unpack_v_planes, analytic_pool_bytes,  # noqa: F401
-                   compress_pool, dequant_pool, dequant_fp16)
+                   compress_pool, dequant_pool, dequant_fp16, append_pool)
 from .attention import (attention_lse, attention_rows, attention_weights, pool_and_tail_decode,  # noqa: F401
                         shared_pool_decode, shared_pool_lse)

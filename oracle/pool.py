@@ -94,3 +94,28 @@ def dequant_fp16(pool: dict, centroids, n_tokens=None):
     """
     k_hat, v_hat = dequant_pool(pool, centroids, n_tokens)
     return k_hat.astype(np.float16), v_hat.astype(np.float16)
+
+
+def append_pool(pool: dict, k_chunk, v_chunk, token_begin: int, boundaries) -> dict:
+    """Write-once compression of one prefill chunk into tokens [token_begin, token_begin + n)
+    of an existing pool of capacity T (PolyKV, Abstract: the cache is compressed a single
+    time; here each chunk of the shared context is compressed once, when it arrives).
+
+    pool: arrays as compress_pool returns them, with "v_codes" [L][H][T][d]; k_chunk and
+    v_chunk: fp16 [L][H][n][d]. Every step of both codecs is per token, so the chunk's
+    codes, scales and norms are those of compress_pool on the chunk alone; the planes are
+    re-packed from the updated codes. Returns a new dict.
+    """
+    n = k_chunk.shape[-2]
+    T = pool["k_codes"].shape[-2]
+    if token_begin < 0 or n < 1 or token_begin + n > T:
+        raise ValueError("token range outside the pool")
+    part = compress_pool(k_chunk, v_chunk, boundaries)
+    out = {key: np.array(val, copy=True) for key, val in pool.items()}
+    sl = slice(token_begin, token_begin + n)
+    out["k_codes"][..., sl, :] = part["k_codes"]
+    out["k_scales"][..., sl, :] = part["k_scales"]
+    out["v_codes"][..., sl, :] = part["v_codes"]
+    out["v_norms"][..., sl] = part["v_norms"]
+    out["v_planes"] = pack_v_planes(out["v_codes"])
+    return out

@@ -196,6 +196,27 @@ def test_dequant_validation(L):
     assert L.polykv_dequant_v(A256, lb, ctypes.byref(cb), A16, 0, 2, None) == -8
 
 
+def test_append_and_prefix_validation(L):
+    lay = _layout()               # 2 layers, capacity n_tokens
+    lb = ctypes.byref(lay)
+    T = lay.shape.n_tokens
+    for f, extra in ((L.polykv_append_k, ()), (L.polykv_append_v, (None,))):
+        def call(tb, n, lbeg=0, lc=2, src=A16, pool=A256):
+            return f(src, pool, lb, *extra, tb, n, lbeg, lc, None)
+        assert call(0, 1, src=None) == -1
+        assert call(0, 1, pool=ctypes.c_void_p(0x20010)) == -3
+        assert call(-1, 2) == -4
+        assert call(0, 0) == -4
+        assert call(T - 3, 4) == -4         # past the capacity
+        assert call(0, T, lbeg=1) == -4
+    cb = pk.polykv_codebook_default()
+    cb.boundary[3] = 0.1
+    assert L.polykv_append_v(A16, A256, lb, ctypes.byref(cb), 0, 1, 0, 2, None) == -8
+    for n_valid in (0, T + 1):
+        assert L.polykv_attend_shared_prefix(A256, lb, None, A16, A16, None, n_valid, 2, 2,
+                                             ctypes.c_float(0.1), 0, 2, None, 0, None, 0) == -4
+
+
 def test_strerror(L):
     for code in range(0, -11, -1):
         assert isinstance(pk.polykv_strerror(code), str) and pk.polykv_strerror(code)

@@ -128,3 +128,30 @@ def test_dequant_fp16_matches_round_trip_bounds():
     assert np.all(err <= s / 2 + np.abs(kh) * 2.0 ** -11 + 1e-12)
     np.testing.assert_array_equal(v16, vh.astype(np.float16))
     assert k16.dtype == np.float16 and v16.dtype == np.float16
+
+
+@pytest.mark.parametrize("order", ["forward", "shuffled"])
+def test_append_in_any_order_equals_one_compress(order):
+    """Chunks written one at a time, in order or not, give the one-shot pool: the codecs
+    work per token (q8_0 blocks lie along head_dim, the rotation and norm are per vector)."""
+    from oracle import append_pool
+    rng = np.random.default_rng(12)
+    L, H, T, d = 2, 2, 101, 64
+    k = rng.standard_normal((L, H, T, d)).astype(np.float16)
+    v = rng.standard_normal((L, H, T, d)).astype(np.float16)
+    _, b32 = codebook_fp32()
+    whole = compress_pool(k, v, b32)
+    cuts = [0, 1, 32, 45, 64, 100, T]
+    chunks = list(zip(cuts[:-1], cuts[1:]))
+    if order == "shuffled":
+        chunks = [chunks[i] for i in (3, 0, 5, 2, 4, 1)]
+    # start from a pool whose every code and norm is something else
+    pool = {"k_codes": np.full_like(whole["k_codes"], 77), "k_scales": np.full_like(whole["k_scales"], 3.0),
+            "v_codes": np.full_like(whole["v_codes"], 5), "v_norms": np.full_like(whole["v_norms"], 9.0)}
+    pool["v_planes"] = pack_v_planes(pool["v_codes"])
+    for a, b in chunks:
+        pool = append_pool(pool, k[..., a:b, :], v[..., a:b, :], a, b32)
+    for key in ("k_codes", "k_scales", "v_codes", "v_norms", "v_planes"):
+        assert np.array_equal(pool[key], whole[key]), key
+    with pytest.raises(ValueError):
+        append_pool(pool, k[..., :5, :], v[..., :5, :], T - 4, b32)
