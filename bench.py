@@ -43,6 +43,8 @@ def _parse():
     p.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
     p.add_argument("--warm", action="store_true", help="one pool copy, left in the caches between launches")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--chunk-tokens", type=int, default=512,
+                   help="prefill chunk size for the append figure")
     p.add_argument("--tail-tokens", type=int, default=None,
                    help="private fp16 tail per agent for the tail-merge figure (default: the decode steps)")
     p.add_argument("--cpu-sample-layers", type=int, default=None)
@@ -183,6 +185,10 @@ def main():
              for _ in range(n_pools)] if n_tail > 0 else []
     tail_len = torch.full((cfg.n_agents,), n_tail, dtype=torch.int32, device=dev)
     lse = torch.empty((cfg.n_layers, cfg.n_agents, cfg.n_q_heads), dtype=torch.float32, device=dev)
+    # Prefill chunks for the append figure: the same context cut into --chunk-tokens pieces
+    chunk = max(1, min(args.chunk_tokens, cfg.n_tokens))
+    cuts = list(range(0, cfg.n_tokens, chunk)) + [cfg.n_tokens]
+    chunks = [(a, b, k[:, :, a:b, :].contiguous(), v[:, :, a:b, :].contiguous()) for a, b in zip(cuts[:-1], cuts[1:])]
     torch.cuda.synchronize()
 
     def ev():
@@ -209,6 +215,12 @@ def main():
             e.append(ev())
         rec.append(e)
 
+    def append_all(i):
+        # the whole context, chunk by chunk, into pool copy i (it ends up identical)
+        for a, b, kc, vc in chunks:
+            pk.polykv_append_k(kc, pools[i % n_pools], lay, a, stream=stream)
+            pk.polykv_append_v(vc, pools[i % n_pools], lay, a, stream=stream)
+
     def dequant(i, which):
         # pool copy i -> fp16 K or V (into the compress inputs, which are not needed again)
         if which == "k":
@@ -230,6 +242,8 @@ def main():
                                             cfg.softmax_scale, path, workspace=ws, stream=stream)
                 for i in range(2 * n_pools):
                     tail_merge(i)
+            for i in range(2 * n_pools):
+                append_all(i)
             for i in range(2 * n_pools):
                 dequant(i, "k")
                 dequant(i, "v")
@@ -276,6 +290,16 @@ def main():
                 if i >= n_pools:
                     tail_ev.append((e0, e1))
             stream.synchronize()
+
+        # Secondary figure: the same compression as prefill chunks appended one at a time.
+        app_ev = []
+        for i in range(n_pools + 6):
+            e0 = ev()
+            append_all(i)
+            e1 = ev()
+            if i >= n_pools:
+                app_ev.append((e0, e1))
+        stream.synchronize()
 
         # Secondary figure: dequantisation of a pool back to fp16 K and V. It runs last,
         # because it overwrites the compress inputs.
@@ -352,6 +376,12 @@ def main():
                                 "frac_hbm": tail_bytes / t_tail / 1e9 / HBM_PEAK_GBPS,
                                 "algorithmic_bytes_per_launch": tail_bytes,
                                 "traffic": _traffic("attend_tail", ["attend_tail.hip"], "%s_tail%d" % (workload, n_tail))}
+    t_app = sum(a.elapsed_time(b) for a, b in app_ev) / len(app_ev) / 1e3
+    result["append"] = {"kernels": ["compress_k", "compress_v"], "chunk_tokens": chunk,
+                        "chunks": len(chunks), "us": t_app * 1e6,
+                        "GBps": compress_bytes / t_app / 1e9,
+                        "frac_hbm": compress_bytes / t_app / 1e9 / HBM_PEAK_GBPS,
+                        "algorithmic_bytes": compress_bytes}
     t_dk = sum(a.elapsed_time(b) for a, b in dq_ev["k"]) / len(dq_ev["k"]) / 1e3
     t_dv = sum(a.elapsed_time(b) for a, b in dq_ev["v"]) / len(dq_ev["v"]) / 1e3
     # algorithmic bytes: the pool's K (or V) region read, fp16 K (or V) written
