@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpolykv.so")
-SOURCES = ["host.cpp", "compress.hip", "attend.hip", "attend_mfma.hip", "attend_tail.hip", "dequant.hip"]
+SOURCES = ["host.cpp", "compress.hip", "attend.hip", "attend_mfma.hip", "attend_tail.hip", "dequant.hip", "project.hip"]
 
 # -packed-fp32-ops: no packed fp32 VALU instructions in device code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -26,7 +26,8 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 # per-file extras: the value compressor keeps matrix-core results in ordinary vector
 # registers (its compares read them directly)
-FILE_FLAGS = {"compress.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"compress.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "project.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc():

@@ -276,6 +276,48 @@ int polykv_append_v(const void* v_fp16, void* pool, const polykv_layout_t* layou
                                                      layer_count, (hipStream_t)hip_stream));
 }
 
+static int check_projection(int32_t n_tok, int32_t hidden, int32_t n_heads, int32_t head_dim) {
+    if (n_tok < 1 || n_heads < 1 || hidden < 64 || hidden % 64 != 0) return POLYKV_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return POLYKV_ERR_SHAPE;
+    return POLYKV_OK;
+}
+
+int polykv_project_kv(const void* x, const void* w_k, const void* w_v, void* k_fp16, void* v_fp16,
+                      int32_t n_tok, int32_t hidden, int32_t n_heads, int32_t head_dim,
+                      void* hip_stream) {
+    if (!x || !w_k || !k_fp16 || (w_v && !v_fp16)) return POLYKV_ERR_NULL;
+    int rc = check_projection(n_tok, hidden, n_heads, head_dim);
+    if (rc) return rc;
+    if (!aligned(x, 16) || !aligned(w_k, 16) || !aligned(k_fp16, 16) ||
+        (w_v && (!aligned(w_v, 16) || !aligned(v_fp16, 16))))
+        return POLYKV_ERR_ALIGN;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_project((const __half*)x, (const __half*)w_k, (const __half*)w_v,
+                                            (__half*)k_fp16, (__half*)v_fp16, n_tok, hidden, n_heads,
+                                            head_dim, (hipStream_t)hip_stream));
+}
+
+int polykv_project_compress(const void* x, const void* w_k, const void* w_v, void* pool,
+                            const polykv_layout_t* layout, const polykv_codebook_t* cb, int32_t layer,
+                            int32_t token_begin, int32_t n_tok, int32_t hidden, void* hip_stream) {
+    if (!x || !w_k || !w_v || !pool || !layout) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if ((rc = check_projection(n_tok, hidden, layout->shape.n_kv_heads, layout->shape.head_dim))) return rc;
+    if (!aligned(pool, 256) || !aligned(x, 16) || !aligned(w_k, 16) || !aligned(w_v, 16))
+        return POLYKV_ERR_ALIGN;
+    if (layer < 0 || layer >= layout->shape.n_layers) return POLYKV_ERR_RANGE;
+    if ((rc = check_tokens(*layout, token_begin, n_tok))) return rc;
+    if (token_begin % 32 != 0) return POLYKV_ERR_RANGE;
+    const polykv_codebook_t& book = cb ? *cb : default_codebook();
+    if (!codebook_ok(book)) return POLYKV_ERR_CODEBOOK;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_project_compress((const __half*)x, (const __half*)w_k, (const __half*)w_v,
+                                                     (uint8_t*)pool, polykv::make_geom(*layout),
+                                                     half_of(book), layer, token_begin, n_tok, hidden,
+                                                     (hipStream_t)hip_stream));
+}
+
 int polykv_dequant_k(const void* pool, const polykv_layout_t* layout, void* k_fp16,
                      int32_t layer_begin, int32_t layer_count, void* hip_stream) {
     if (!pool || !layout || !k_fp16) return POLYKV_ERR_NULL;

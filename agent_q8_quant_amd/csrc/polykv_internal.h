@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
 #include <stdint.h>
 
 #include "polykv.h"
@@ -86,6 +87,16 @@ struct TailArgs {
     float softmax_scale;
 };
 hipError_t launch_attend_tail(const TailArgs& a, hipStream_t s);
+
+// K/V projection x W^T (project.hip): fp16 [n_heads][n_tok][d] outputs (w_v may be NULL),
+// or compressed straight into pool layer `layer`, tokens [tok0, tok0 + n_tok).
+hipError_t launch_project(const __half* x, const __half* w_k, const __half* w_v, __half* k_out,
+                          __half* v_out, int32_t n_tok, int32_t hidden, int32_t n_heads,
+                          int32_t head_dim, hipStream_t s);
+hipError_t launch_project_compress(const __half* x, const __half* w_k, const __half* w_v,
+                                   uint8_t* pool, const PoolGeom& g, const CodebookHalf& cb,
+                                   int32_t layer, int32_t tok0, int32_t n_tok, int32_t hidden,
+                                   hipStream_t s);
 
 // Pool -> fp16 K / V (dequant.hip).
 hipError_t launch_dequant_k(const uint8_t* pool, void* k_fp16, const PoolGeom& g,

@@ -21,7 +21,8 @@ EXPORTED_SYMBOLS = (
     "polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k", "polykv_compress_v",
     "polykv_attend_workspace_bytes", "polykv_attend_path", "polykv_attend_shared", "polykv_attend_shared_path",
     "polykv_attend_shared_lse", "polykv_attend_shared_prefix", "polykv_attend_tail_merge",
-    "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v", "polykv_strerror",
+    "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v",
+    "polykv_project_kv", "polykv_project_compress", "polykv_strerror",
 )
 
 
@@ -66,6 +67,9 @@ def lib():
         L.polykv_compress_v.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t),
                                         ctypes.POINTER(polykv_codebook_t), i32, i32, vp]
         L.polykv_dequant_k.argtypes = [vp, ctypes.POINTER(polykv_layout_t), vp, i32, i32, vp]
+        L.polykv_project_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        L.polykv_project_compress.argtypes = [vp, vp, vp, vp, ctypes.POINTER(polykv_layout_t),
+                                              ctypes.POINTER(polykv_codebook_t), i32, i32, i32, i32, vp]
         L.polykv_dequant_v.argtypes = [vp, ctypes.POINTER(polykv_layout_t), ctypes.POINTER(polykv_codebook_t),
                                        vp, i32, i32, vp]
         L.polykv_attend_workspace_bytes.argtypes = [ctypes.POINTER(polykv_layout_t), i32, i32, i32]
@@ -88,7 +92,8 @@ def lib():
         for name in ("polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k",
                      "polykv_compress_v", "polykv_attend_shared", "polykv_attend_shared_path",
                      "polykv_attend_shared_lse", "polykv_attend_shared_prefix", "polykv_attend_tail_merge",
-                     "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v"):
+                     "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v",
+                     "polykv_project_kv", "polykv_project_compress"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -190,6 +195,35 @@ def polykv_append_v(v, pool, layout, token_begin, n_new=None, cb=None, layer_beg
                                ctypes.byref(cb) if cb is not None else None, int(token_begin), n_new, lb, lc,
                                _stream_ptr(stream))
     _check(rc, "polykv_append_v")
+
+
+def polykv_project_kv(x, w_k, w_v, k, v, n_heads, head_dim, stream=None):
+    """fp16 K (and V) = RNE16(x W^T), head-major [n_heads][n_tok][head_dim]."""
+    n_tok, hidden = int(x.shape[0]), int(x.shape[1])
+    if x.dim() != 2 or w_k.shape != (n_heads * head_dim, hidden) or k.numel() != n_heads * n_tok * head_dim:
+        raise ValueError("x, w_k or k has the wrong shape")
+    if w_v is not None and (w_v.shape != w_k.shape or v is None or v.numel() != k.numel()):
+        raise ValueError("w_v or v has the wrong shape")
+    rc = lib().polykv_project_kv(_dev(x, torch.float16, "x"), _dev(w_k, torch.float16, "w_k"),
+                                 _dev(w_v, torch.float16, "w_v") if w_v is not None else None,
+                                 _dev(k, torch.float16, "k"), _dev(v, torch.float16, "v") if w_v is not None else None,
+                                 n_tok, hidden, int(n_heads), int(head_dim), _stream_ptr(stream))
+    _check(rc, "polykv_project_kv")
+
+
+def polykv_project_compress(x, w_k, w_v, pool, layout, layer, token_begin, cb=None, stream=None):
+    """Project x [n_tok][hidden] with w_k, w_v [H*d][hidden] and compress into the pool."""
+    n_tok, hidden = int(x.shape[0]), int(x.shape[1])
+    s = layout.shape
+    if x.dim() != 2 or w_k.shape != (s.n_kv_heads * s.head_dim, hidden) or w_v.shape != w_k.shape:
+        raise ValueError("x, w_k or w_v has the wrong shape")
+    if pool.numel() < layout.total_bytes:
+        raise ValueError("pool has the wrong size for the layout")
+    rc = lib().polykv_project_compress(_dev(x, torch.float16, "x"), _dev(w_k, torch.float16, "w_k"),
+                                       _dev(w_v, torch.float16, "w_v"), _dev(pool, torch.uint8, "pool"),
+                                       ctypes.byref(layout), ctypes.byref(cb) if cb is not None else None,
+                                       int(layer), int(token_begin), n_tok, hidden, _stream_ptr(stream))
+    _check(rc, "polykv_project_compress")
 
 
 def polykv_dequant_k(pool, layout, k, layer_begin=0, layer_count=None, stream=None):

@@ -221,6 +221,31 @@ def main():
             pk.polykv_append_k(kc, pools[i % n_pools], lay, a, stream=stream)
             pk.polykv_append_v(vc, pools[i % n_pools], lay, a, stream=stream)
 
+    # Fused K/V projection + compression (prefill): one layer's input rows x [T][hidden] and
+    # the two projection weights [H*d][hidden], seeded normals (random weights, as no
+    # checkpoint is used); hidden = the model's width (query heads x head_dim).
+    hidden = cfg.n_q_heads * cfg.head_dim
+    proj = None
+    if cfg.head_dim in (64, 128) and hidden % 64 == 0:
+        px = torch.randn((cfg.n_tokens, hidden), generator=gen, device=dev).to(torch.float16)
+        pwk = (torch.randn((cfg.n_kv_heads * cfg.head_dim, hidden), generator=gen, device=dev) / hidden ** 0.5).to(torch.float16)
+        pwv = (torch.randn((cfg.n_kv_heads * cfg.head_dim, hidden), generator=gen, device=dev) / hidden ** 0.5).to(torch.float16)
+        pk_tmp = torch.empty((cfg.n_kv_heads, cfg.n_tokens, cfg.head_dim), dtype=torch.float16, device=dev)
+        pv_tmp = torch.empty_like(pk_tmp)
+        proj = (px, pwk, pwv, pk_tmp, pv_tmp)
+
+    def project_fused(i):
+        px, pwk, pwv, _, _ = proj
+        for l in range(cfg.n_layers):
+            pk.polykv_project_compress(px, pwk, pwv, pools[i % n_pools], lay, l, 0, stream=stream)
+
+    def project_unfused(i):
+        px, pwk, pwv, kt, vt = proj
+        for l in range(cfg.n_layers):
+            pk.polykv_project_kv(px, pwk, pwv, kt, vt, cfg.n_kv_heads, cfg.head_dim, stream=stream)
+            pk.polykv_append_k(kt, pools[i % n_pools], lay, 0, layer_begin=l, layer_count=1, stream=stream)
+            pk.polykv_append_v(vt, pools[i % n_pools], lay, 0, layer_begin=l, layer_count=1, stream=stream)
+
     def dequant(i, which):
         # pool copy i -> fp16 K or V (into the compress inputs, which are not needed again)
         if which == "k":
@@ -300,6 +325,20 @@ def main():
             if i >= n_pools:
                 app_ev.append((e0, e1))
         stream.synchronize()
+
+        # Secondary figure: the K/V projection of every layer with the compression fused in,
+        # against the projection written as fp16 and then appended (the same pool bytes).
+        # The pools end up holding the projected cache; nothing after this reads them.
+        pj_ev = {"fused": [], "unfused": []}
+        if proj is not None:
+            for name, fn in (("fused", project_fused), ("unfused", project_unfused)):
+                fn(0)
+                for i in range(2):
+                    e0 = ev()
+                    fn(i)
+                    e1 = ev()
+                    pj_ev[name].append((e0, e1))
+            stream.synchronize()
 
         # Secondary figure: dequantisation of a pool back to fp16 K and V. It runs last,
         # because it overwrites the compress inputs.
@@ -382,6 +421,16 @@ def main():
                         "GBps": compress_bytes / t_app / 1e9,
                         "frac_hbm": compress_bytes / t_app / 1e9 / HBM_PEAK_GBPS,
                         "algorithmic_bytes": compress_bytes}
+    if pj_ev["fused"]:
+        t_f = sum(a.elapsed_time(b) for a, b in pj_ev["fused"]) / len(pj_ev["fused"]) / 1e3
+        t_u = sum(a.elapsed_time(b) for a, b in pj_ev["unfused"]) / len(pj_ev["unfused"]) / 1e3
+        flops = 2.0 * cfg.n_layers * cfg.n_tokens * hidden * 2 * cfg.n_kv_heads * cfg.head_dim
+        result["project_compress"] = {
+            "kernel": "project (fused)", "hidden": hidden, "layers": cfg.n_layers,
+            "us_fused": t_f * 1e6, "us_unfused": t_u * 1e6,
+            "roofline": {"bound": "mfma", "achieved": flops / t_f / 1e12, "peak": 2500.0,
+                         "unit": "TFLOP/s", "frac": flops / t_f / 1e12 / 2500.0},
+            "flops": flops}
     t_dk = sum(a.elapsed_time(b) for a, b in dq_ev["k"]) / len(dq_ev["k"]) / 1e3
     t_dv = sum(a.elapsed_time(b) for a, b in dq_ev["v"]) / len(dq_ev["v"]) / 1e3
     # algorithmic bytes: the pool's K (or V) region read, fp16 K (or V) written

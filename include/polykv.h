@@ -156,6 +156,38 @@ int polykv_append_v(const void* v_fp16, void* pool, const polykv_layout_t* layou
                     int32_t layer_begin, int32_t layer_count, void* hip_stream);
 
 /*
+ * K/V projection of one layer's prefill chunk, with the pool compression fused into its
+ * epilogue. PolyKV, Abstract: the shared cache is compressed a single time, as it is
+ * written; here that happens where K and V are produced, so they never reach HBM as fp16.
+ *   K = RNE16(x W_k^T), V = RNE16(x W_v^T)    (fp16 operands, fp32 accumulation)
+ * each rounded to fp16 as an fp16 cache would hold it, then compressed exactly as
+ * polykv_append_k/v would compress those fp16 values (so the pool bytes equal those of
+ * polykv_project_kv followed by polykv_append_k/v).
+ *  x:        device fp16 [n_tok][hidden], row-major, 16-B aligned (the layer's input rows).
+ *  w_k, w_v: device fp16 [n_kv_heads * head_dim][hidden], row-major (a linear layer's weight
+ *            [out][in]); output j is dim j % head_dim of KV head j / head_dim.
+ *  pool:     device, layout->total_bytes, 256-B aligned; layer `layer`, tokens
+ *            [token_begin, token_begin + n_tok) are written (token_begin a multiple of 32;
+ *            plane bits of later tokens below the capacity in the last group are kept).
+ *  hidden:   a multiple of 64; head_dim 64 or 128.
+ * Errors: NULL, SHAPE, ALIGN, RANGE (layer, token range, token_begin % 32), LAYOUT,
+ *         CODEBOOK, DEVICE, LAUNCH.
+ */
+int polykv_project_compress(const void* x, const void* w_k, const void* w_v, void* pool,
+                            const polykv_layout_t* layout, const polykv_codebook_t* cb,
+                            int32_t layer, int32_t token_begin, int32_t n_tok, int32_t hidden,
+                            void* hip_stream);
+
+/*
+ * The same projection without the compression: k_fp16 (and v_fp16 when w_v is not NULL)
+ * receive RNE16(x W^T) head-major, [n_heads][n_tok][head_dim] (16-B aligned), the input
+ * layout of polykv_append_k/v for one layer. Errors: NULL, SHAPE, ALIGN, DEVICE, LAUNCH.
+ */
+int polykv_project_kv(const void* x, const void* w_k, const void* w_v, void* k_fp16, void* v_fp16,
+                      int32_t n_tok, int32_t hidden, int32_t n_heads, int32_t head_dim,
+                      void* hip_stream);
+
+/*
  * Pool -> fp16 keys. PolyKV, Abstract: the shared pool is handed to each agent as an
  * ordinary per-layer KV cache; this reconstructs the keys of layers
  * [layer_begin, layer_begin + layer_count):

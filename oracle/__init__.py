@@ -34,3 +34,4 @@ from .pool import (pack_v_planes, unpack_v_planes, analytic_pool_bytes,  # noqa:
                    compress_pool, dequant_pool, dequant_fp16, append_pool)
 from .attention import (attention_lse, attention_rows, attention_weights, pool_and_tail_decode,  # noqa: F401
                         shared_pool_decode, shared_pool_lse)
+from .project import project_fp16, project_fp64  # noqa: F401

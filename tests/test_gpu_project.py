@@ -1,0 +1,105 @@
+"""Fused K/V projection + compression on the GPU, through the C ABI.
+
+- The plain projection (polykv_project_kv) against the oracle's fp64 projection: the GPU
+  sums exact fp16 x fp16 products in fp32, so its sum y lies within
+  E = hidden * 2^-24 * sum_k |x_k w_k| of the exact x (any order of fp32 additions, with a
+  little slack for the order-dependent gamma term); rounding to nearest is monotone, so the
+  fp16 result lies between RNE16(x - E) and RNE16(x + E).
+- The fused kernel (polykv_project_compress) writes exactly the pool bytes of the plain
+  projection followed by polykv_append_k/v (the same accumulators are rounded to fp16 and
+  the same codecs run on them), into a garbage-filled pool, for chunks that start at a
+  multiple of 32 and have ragged lengths; every byte outside the chunk is left alone.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import agent_q8_quant_amd as pk
+import oracle
+from gpu_helpers import device, new_pool
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(n_tok, hidden, H, d, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n_tok, hidden)).astype(np.float16)
+    wk = (rng.standard_normal((H * d, hidden)) / np.sqrt(hidden)).astype(np.float16)
+    wv = (rng.standard_normal((H * d, hidden)) / np.sqrt(hidden)).astype(np.float16)
+    return x, wk, wv
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device())
+
+
+def check_projection(got16, x, w, H, d):
+    exact = oracle.project_fp64(x, w, H, d)
+    absum = oracle.project_fp64(np.abs(x.astype(np.float64)), np.abs(w.astype(np.float64)), H, d)
+    E = x.shape[1] * 2.0 ** -24 * absum * 1.01 + 1e-30
+    lo = (exact - E).astype(np.float16).astype(np.float64)
+    hi = (exact + E).astype(np.float16).astype(np.float64)
+    g = np.asarray(got16, dtype=np.float64).reshape(exact.shape)
+    assert np.all((lo <= g) & (g <= hi)), "projection outside the fp32 summation bound"
+    return int(np.sum(g != exact.astype(np.float16).astype(np.float64)))
+
+
+@pytest.mark.parametrize("shape", [(100, 64, 3, 64), (300, 256, 2, 128), (128, 512, 1, 128), (33, 128, 4, 64)],
+                         ids=lambda s: "n%dK%dH%dd%d" % s)
+def test_plain_projection(shape):
+    n, hidden, H, d = shape
+    print("project", shape, flush=True)
+    x, wk, wv = _inputs(n, hidden, H, d, seed=n + hidden)
+    k = torch.full((H, n, d), float("nan"), dtype=torch.float16, device=device())
+    v = torch.full_like(k, float("nan"))
+    pk.polykv_project_kv(_dev(x), _dev(wk), _dev(wv), k, v, H, d)
+    torch.cuda.synchronize()
+    nk = check_projection(k.cpu().numpy(), x, wk, H, d)
+    nv = check_projection(v.cpu().numpy(), x, wv, H, d)
+    assert nk + nv <= 0.01 * 2 * k.numel()
+    # K only
+    k2 = torch.empty_like(k)
+    pk.polykv_project_kv(_dev(x), _dev(wk), None, k2, None, H, d)
+    torch.cuda.synchronize()
+    assert torch.equal(k2, k)
+
+
+@pytest.mark.parametrize("case", [(2, 3, 64, 300, 256, 0, 300, 1), (2, 2, 128, 600, 128, 64, 100, 0),
+                                  (1, 1, 128, 256, 64, 128, 128, 0), (1, 2, 64, 97, 512, 32, 65, 0)],
+                         ids=lambda c: "L%dH%dd%dT%dK%d_at%d_n%d_l%d" % c)
+def test_fused_equals_projection_then_append(case):
+    L, H, d, T, hidden, tb, n, layer = case
+    print("fused", case, flush=True)
+    x, wk, wv = _inputs(n, hidden, H, d, seed=T + n)
+    lay = pk.polykv_pool_layout(L, H, d, T)
+    rng = np.random.default_rng(7)
+    img = rng.integers(0, 256, lay.total_bytes, dtype=np.uint8)
+    fused = torch.from_numpy(img.copy()).to(device())
+    plain = torch.from_numpy(img.copy()).to(device())
+    xd, wkd, wvd = _dev(x), _dev(wk), _dev(wv)
+    pk.polykv_project_compress(xd, wkd, wvd, fused, lay, layer, tb)
+    k = torch.empty((H, n, d), dtype=torch.float16, device=device())
+    v = torch.empty_like(k)
+    pk.polykv_project_kv(xd, wkd, wvd, k, v, H, d)
+    pk.polykv_append_k(k, plain, lay, tb, layer_begin=layer, layer_count=1)
+    pk.polykv_append_v(v, plain, lay, tb, layer_begin=layer, layer_count=1)
+    torch.cuda.synchronize()
+    a, b = fused.cpu().numpy(), plain.cpu().numpy()
+    assert np.array_equal(a, b), "fused pool differs from projection + append at %d bytes" % int(np.sum(a != b))
+    assert not np.array_equal(a, img)
+
+
+def test_fused_rejects_unaligned_chunks_and_bad_shapes():
+    lay = pk.polykv_pool_layout(1, 1, 128, 128)
+    pool = new_pool(lay)
+    x = torch.zeros((40, 64), dtype=torch.float16, device=device())
+    w = torch.zeros((128, 64), dtype=torch.float16, device=device())
+    with pytest.raises(pk.PolyKVError):
+        pk.polykv_project_compress(x, w, w, pool, lay, 0, 16)       # token_begin % 32 != 0
+    with pytest.raises(pk.PolyKVError):
+        pk.polykv_project_compress(x, w, w, pool, lay, 0, 96)       # past the capacity
+    x2 = torch.zeros((40, 48), dtype=torch.float16, device=device())
+    w2 = torch.zeros((128, 48), dtype=torch.float16, device=device())
+    with pytest.raises(pk.PolyKVError):
+        pk.polykv_project_compress(x2, w2, w2, pool, lay, 0, 0)     # hidden not a multiple of 64

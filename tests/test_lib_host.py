@@ -217,6 +217,32 @@ def test_append_and_prefix_validation(L):
                                              ctypes.c_float(0.1), 0, 2, None, 0, None, 0) == -4
 
 
+def test_projection_validation(L):
+    lay = _layout()
+    lb = ctypes.byref(lay)
+    H, d, T = lay.shape.n_kv_heads, lay.shape.head_dim, lay.shape.n_tokens
+
+    def fused(x=A16, wk=A16, wv=A16, pool=A256, layer=0, tb=0, n=32, hidden=128, cb=None):
+        return L.polykv_project_compress(x, wk, wv, pool, lb, cb, layer, tb, n, hidden, None)
+    assert fused(x=None) == -1
+    assert fused(wv=None) == -1
+    assert fused(hidden=96) == -2          # not a multiple of 64
+    assert fused(n=0) == -2
+    assert fused(x=ctypes.c_void_p(0x10008)) == -3
+    assert fused(pool=ctypes.c_void_p(0x20010)) == -3
+    assert fused(layer=2) == -4
+    assert fused(tb=16) == -4              # chunks start at a multiple of 32
+    assert fused(tb=32, n=T) == -4         # past the capacity
+
+    def plain(x=A16, wk=A16, wv=None, k=A16, v=None, n=8, hidden=64, heads=H, hd=d):
+        return L.polykv_project_kv(x, wk, wv, k, v, n, hidden, heads, hd, None)
+    assert plain(k=None) == -1
+    assert plain(wv=A16, v=None) == -1     # V output missing
+    assert plain(hd=32) == -2
+    assert plain(heads=0) == -2
+    assert plain(k=ctypes.c_void_p(0x10004)) == -3
+
+
 def test_strerror(L):
     for code in range(0, -11, -1):
         assert isinstance(pk.polykv_strerror(code), str) and pk.polykv_strerror(code)
