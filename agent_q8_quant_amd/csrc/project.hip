@@ -12,9 +12,9 @@
 // Work layout: one workgroup per (128-token tile, head, K or V), four waves; wave w owns
 // tokens 32 w .. 32 w + 31 of the tile and all d columns of the head. The reduction over
 // the hidden size runs in 64-wide steps: both operand tiles ([128 tokens][64] of x and
-// [d outputs][64] of W, k-contiguous, 16-byte pieces XOR-swizzled by row) go through LDS,
-// and every thread holds the next step's pieces in registers while the current step is
-// multiplied (v_mfma_f32_32x32x16_f16: 32 tokens x 32 outputs per instruction, fp16
+// [d outputs][64] of W, k-contiguous, 16-byte pieces XOR-swizzled by row) go through two
+// LDS stages, and every thread holds the pieces of the step after next in registers while
+// the current step is multiplied (v_mfma_f32_32x32x16_f16: 32 tokens x 32 outputs per instruction, fp16
 // operands, fp32 accumulation). After the last step each wave rounds its 32 x d block to
 // fp16 into LDS and encodes it: keys with the q8_0 codec (one lane per 8 entries), values
 // with the matrix-core TurboQuant codec (the wave's 32 tokens are one 32-token group).
@@ -42,10 +42,11 @@ struct PjCfg {
     static constexpr int W_PIECES = D * BK / 8;
     static constexpr int XPT = X_PIECES / 256;        // per thread
     static constexpr int WPT = W_PIECES / 256;
-    static constexpr int OFF_X = 0;
+    static constexpr int OFF_X = 0;                                  // two stages of x and W
     static constexpr int OFF_W = OFF_X + BM * BK * 2;
-    static constexpr int LDS_MAIN = OFF_W + D * BK * 2;
-    static constexpr int STAGE = 32 * D * 2;          // one wave's fp16 block
+    static constexpr int STAGE_BYTES = OFF_W + D * BK * 2;
+    static constexpr int LDS_MAIN = 2 * STAGE_BYTES;
+    static constexpr int STAGE = 32 * D * 2;          // one wave's fp16 block (epilogue)
     static constexpr int LDS = LDS_MAIN > 4 * STAGE ? LDS_MAIN : 4 * STAGE;
     static_assert(XPT >= 1 && WPT >= 1, "whole pieces per thread");
 };
@@ -99,37 +100,48 @@ __global__ __launch_bounds__(256) void k_project(PjArgs a) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f16v{};
 
+    // two LDS stages: step ks multiplies stage ks % 2 while the registers of step ks + 1 go
+    // into the other stage and the loads of step ks + 2 are in flight; one barrier per step
     const int steps = hidden / BK;
-    fetch(0);
-    for (int ks = 0; ks < steps; ++ks) {
-        __syncthreads();   // the previous step's operands are consumed
+    auto put = [&](int st) {
+        uint8_t* base = lds + st * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::XPT; ++i) {
             const int p = tid + 256 * i;
-            *reinterpret_cast<u4*>(lds + C::OFF_X + sw_off(p >> 3, p & 7)) = px[i];
+            *reinterpret_cast<u4*>(base + C::OFF_X + sw_off(p >> 3, p & 7)) = px[i];
         }
 #pragma unroll
         for (int i = 0; i < C::WPT; ++i) {
             const int p = tid + 256 * i;
-            *reinterpret_cast<u4*>(lds + C::OFF_W + sw_off(p >> 3, p & 7)) = pw[i];
+            *reinterpret_cast<u4*>(base + C::OFF_W + sw_off(p >> 3, p & 7)) = pw[i];
         }
-        __syncthreads();
-        if (ks + 1 < steps) fetch((ks + 1) * BK);   // in flight during the products
+    };
+    fetch(0);
+    put(0);
+    if (steps > 1) fetch(BK);
+    __syncthreads();
+    for (int ks = 0; ks < steps; ++ks) {
+        const uint8_t* base = lds + (ks & 1) * C::STAGE_BYTES;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
             // lane l: row l % 32 of its block, k = 16 s + 8 (l / 32) .. + 7 (piece 2 s + l / 32)
             const uint32_t c = 2u * s + (uint32_t)(lane >> 5);
-            const h8 av = *reinterpret_cast<const h8*>(lds + C::OFF_X + sw_off(32u * w + (lane & 31), c));
+            const h8 av = *reinterpret_cast<const h8*>(base + C::OFF_X + sw_off(32u * w + (lane & 31), c));
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                const h8 bv = *reinterpret_cast<const h8*>(lds + C::OFF_W + sw_off(32u * j + (lane & 31), c));
+                const h8 bv = *reinterpret_cast<const h8*>(base + C::OFF_W + sw_off(32u * j + (lane & 31), c));
                 acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[j], 0, 0, 0);
             }
         }
+        if (ks + 1 < steps) {
+            put((ks + 1) & 1);                          // its readers finished before the last barrier
+            if (ks + 2 < steps) fetch((ks + 2) * BK);
+        }
+        __syncthreads();
     }
 
-    // ---- epilogue: the wave's 32 x D block, rounded to fp16, into its LDS stage ----
-    __syncthreads();   // every wave is done with the operand tiles
+    // ---- epilogue: the wave's 32 x D block, rounded to fp16, into its LDS stage (the
+    // loop's last barrier: every wave is done with the operand tiles) ----
     __half* stage = reinterpret_cast<__half*>(lds + w * C::STAGE);   // [32 tokens][D]
 #pragma unroll
     for (int j = 0; j < NT; ++j)
