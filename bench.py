@@ -267,8 +267,10 @@ def main():
                                             cfg.softmax_scale, path, workspace=ws, stream=stream)
                 for i in range(2 * n_pools):
                     tail_merge(i)
-            for i in range(2 * n_pools):
-                append_all(i)
+            # (appends run the compress kernels on smaller ranges: left out here, so that the
+            # compress kernels' statistics stay those of the one-shot compress)
+            if proj is not None:
+                project_fused(0)
             for i in range(2 * n_pools):
                 dequant(i, "k")
                 dequant(i, "v")
