@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256) void k_dequant_k(const uint8_t* __restrict__ p
 // 2. lane l reads, per coordinate, the three words of its half and takes bit l % 32 of
 //    each: the code, whose centroid comes from an 8-entry LDS table;
 // 3. the FWHT runs in registers over the lane's coordinates, and for d >= 128 one last
-//    butterfly pairs lane l with lane l ^ 32 (the other coordinate half);
+//    butterfly pairs lane l with lane l ^ 32 (the other coordinate half), one register
+//    swap per two coordinates;
 // 4. times n / d, rounded to fp16, stored as 16-byte pieces.
 // ---------------------------------------------------------------------------------------
 template <int D>
@@ -194,29 +195,42 @@ __global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ p
                     x[e] = a + b;
                     x[e + h] = a - b;
                 }
-        if constexpr (C::HALVES == 2) {
-            // coordinate bit log2(d/2): lower half (a) and upper half (b) of the same token
-            const float sgn = half ? -1.0f : 1.0f;
+        // 4. scale by n / d and store 16-byte pieces of `n` consecutive coordinates
+        auto store = [&](const float* v, int first, int n) {
+            u4* o = reinterpret_cast<u4*>(out + ((size_t)cur.tile_local * T + cur.token) * D + first);
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                const uint32_t u = __float_as_uint(x[e]);
-                const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-                // sw[0]: the lower half's value in every lane, sw[1]: the upper half's
-                x[e] = __builtin_fmaf(sgn, __uint_as_float(sw[1]), __uint_as_float(sw[0]));
-            }
-        }
-        // 4. scale by n / d and store
-        if (cur.valid) {
-            u4* o = reinterpret_cast<u4*>(out + ((size_t)cur.tile_local * T + cur.token) * D + coord0);
-#pragma unroll
-            for (int c = 0; c < CPL; c += 8) {
+            for (int c = 0; c < n; c += 8) {
                 uint32_t q[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    q[e] = (uint32_t)__half_as_ushort(__float2half_rn(x[c + 2 * e] * f)) |
-                           ((uint32_t)__half_as_ushort(__float2half_rn(x[c + 2 * e + 1] * f)) << 16);
+                    q[e] = (uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e] * f)) |
+                           ((uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e + 1] * f)) << 16);
                 o[c / 8] = u4{q[0], q[1], q[2], q[3]};
             }
+        };
+        if constexpr (C::HALVES == 2) {
+            // the last butterfly pairs coordinate i (lane l, lower half) with i + d/2 (lane
+            // l ^ 32). One swap of registers e and e + HP (HP = d/4) hands the lower lane both
+            // values of coordinate e and the upper lane both values of coordinate e + HP:
+            // sw[0] is the lower half's value and sw[1] the upper half's in either lane. So
+            // lane l finishes coordinates base + e and base + e + d/2 (e < HP), base = HP for
+            // the upper lane: one swap and two additions per pair.
+            constexpr int HP = CPL / 2;
+            float lo[HP], hi[HP];
+#pragma unroll
+            for (int e = 0; e < HP; ++e) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[e]), __float_as_uint(x[e + HP]), false, false);
+                const float a = __uint_as_float(sw[0]), b = __uint_as_float(sw[1]);
+                lo[e] = a + b;
+                hi[e] = a - b;
+            }
+            if (cur.valid) {
+                const int base = half * HP;
+                store(lo, base, HP);
+                store(hi, base + CPL, HP);
+            }
+        } else {
+            if (cur.valid) store(x, coord0, CPL);
         }
         if (next >= n_items) break;
         item = next;
