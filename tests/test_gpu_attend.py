@@ -277,3 +277,35 @@ def test_determinism_stream_and_layer_range(path):
     pk.polykv_attend_shared_path(pool, lay, q[5:9].contiguous(), lo, cfg.n_agents, cfg.gqa,
                                  cfg.softmax_scale, path, layer_begin=5, layer_count=4)
     assert torch.equal(lo, outs[0][5:9])
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["valu", "mfma"])
+def test_long_context_single_tile(path):
+    """A 100,000-token tile (far past the pages' 7,194): offsets, chunk counts and the
+    streams' merge at a length no workload reaches; the pool is compressed on the GPU and
+    compared with the oracle's compress (keys bit-exact) before the decode is checked."""
+    _supported(path, CONFIGS[0])
+    L, H, d, T = 1, 1, 128, 100_000
+    A, G = 5, 4
+    rng = np.random.default_rng(99)
+    k = rng.standard_normal((L, H, T, d)).astype(np.float16)
+    v = rng.standard_normal((L, H, T, d)).astype(np.float16)
+    lay = pk.polykv_pool_layout(L, H, d, T)
+    pool = new_pool(lay)
+    pk.polykv_compress_k(torch.from_numpy(k).to(device()), pool, lay)
+    pk.polykv_compress_v(torch.from_numpy(v).to(device()), pool, lay)
+    qn = rng.standard_normal((L, A, H * G, d)).astype(np.float32)
+    q = torch.from_numpy(qn).to(device())
+    out = torch.full_like(q, float("nan"))
+    pk.polykv_attend_shared_path(pool, lay, q, out, A, G, d ** -0.5, path)
+    torch.cuda.synchronize()
+    op = oracle.compress_pool(k, v, B32)
+    got = read_pool(pool, lay)
+    assert np.array_equal(got["k_codes"].reshape(op["k_codes"].shape), op["k_codes"])
+    # decode on the GPU's own pool (its value codes may differ from the oracle's only in
+    # the permitted boundary cases), reconstructed by the oracle
+    gp = {"k_codes": got["k_codes"].reshape(L, H, T, d), "k_scales": got["k_scales"].reshape(L, H, T, d // 32),
+          "v_planes": got["v_planes"].reshape(L, H, -1, 3, d), "v_norms": got["v_norms"].reshape(L, H, T)}
+    kh, vh = oracle.dequant_pool(gp, C32, T)
+    ref = oracle.shared_pool_decode(qn, kh, vh, G, d ** -0.5)
+    assert row_rel_err(out.cpu().numpy(), ref) <= DECODE_REL_TOL
