@@ -347,8 +347,7 @@ int polykv_dequant_v(const void* pool, const polykv_layout_t* layout, const poly
 
 static int resolve_path(const polykv::PoolGeom& g, int32_t rows, int32_t path) {
     if (path == POLYKV_PATH_AUTO)
-        return polykv::attend_mfma_supported(g, rows) && rows > 16 ? POLYKV_PATH_MFMA
-                                                                   : POLYKV_PATH_VALU;
+        return polykv::attend_mfma_supported(g, rows) ? POLYKV_PATH_MFMA : POLYKV_PATH_VALU;
     return path;
 }
 

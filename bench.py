@@ -298,7 +298,7 @@ def main():
             for s in range(4):
                 flush.add_(1)
                 e0 = ev()
-                decode(0, s)
+                decode(0, s % D)
                 e1 = ev()
                 cold_us.append((e0, e1))
             stream.synchronize()

@@ -215,7 +215,7 @@ int polykv_dequant_v(const void* pool, const polykv_layout_t* layout, const poly
                      void* v_fp16, int32_t layer_begin, int32_t layer_count, void* hip_stream);
 
 /* Decode kernel choice for polykv_attend_shared_path. */
-#define POLYKV_PATH_AUTO 0   /* the library's choice for the row count                    */
+#define POLYKV_PATH_AUTO 0   /* matrix cores where supported (head_dim 64/128), else VALU */
 #define POLYKV_PATH_VALU 1   /* fp32 vector-ALU contraction                               */
 #define POLYKV_PATH_MFMA 2   /* matrix-core contraction (fp16 operands, fp32 accumulate)  */
 

@@ -133,11 +133,13 @@ def test_attend_validation(L):
 
 
 def test_attend_path_choice(L):
-    """The automatic choice: matrix cores for more than one 16-row MFMA tile of query rows
-    at head_dim 64/128, the vector-ALU kernel otherwise."""
+    """The automatic choice: the matrix-core kernel wherever it applies (head_dim 64/128; it
+    is faster than the vector-ALU kernel at every row count measured, 1 to 60), the
+    vector-ALU kernel otherwise."""
     for d, rows, want in ((128, 60, pk.POLYKV_PATH_MFMA), (64, 17, pk.POLYKV_PATH_MFMA),
-                          (128, 16, pk.POLYKV_PATH_VALU), (128, 1, pk.POLYKV_PATH_VALU),
-                          (256, 60, pk.POLYKV_PATH_VALU)):
+                          (128, 16, pk.POLYKV_PATH_MFMA), (128, 1, pk.POLYKV_PATH_MFMA),
+                          (64, 5, pk.POLYKV_PATH_MFMA), (256, 60, pk.POLYKV_PATH_VALU),
+                          (256, 1, pk.POLYKV_PATH_VALU)):
         lay = pk.polykv_pool_layout(2, 2, d, 100)
         assert pk.polykv_attend_path(lay, rows, 1) == want, (d, rows)
     lay = _layout()
