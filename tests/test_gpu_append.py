@@ -156,3 +156,26 @@ def test_prefix_range_errors():
     for bad in (0, T + 1):
         with pytest.raises(pk.PolyKVError):
             pk.polykv_attend_shared_prefix(pool, lay, q, out, None, bad, 1, 1, 0.1)
+
+
+def test_append_full_size_equals_one_shot():
+    """The 4K Llama-3-8B context appended as eight 512-token chunks (the benchmark's append
+    figure) gives the one-shot pool byte for byte."""
+    from gpu_helpers import layout_for, upload_kv
+    from workloads import CONFIGS
+    cfg = CONFIGS[3]
+    print("append full size", flush=True)
+    lay = layout_for(cfg)
+    k, v = upload_kv(cfg)
+    one = new_pool(lay, fill=0x00)
+    pk.polykv_compress_k(k, one, lay)
+    pk.polykv_compress_v(v, one, lay)
+    app = new_pool(lay, fill=0xC3)
+    for a in range(0, cfg.n_tokens, 512):
+        b = min(a + 512, cfg.n_tokens)
+        pk.polykv_append_k(k[:, :, a:b, :].contiguous(), app, lay, a)
+        pk.polykv_append_v(v[:, :, a:b, :].contiguous(), app, lay, a)
+    torch.cuda.synchronize()
+    got, want = pk.pool_views(app, lay), pk.pool_views(one, lay)
+    for key in want:
+        assert torch.equal(got[key], want[key]), key

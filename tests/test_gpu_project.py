@@ -103,3 +103,29 @@ def test_fused_rejects_unaligned_chunks_and_bad_shapes():
     w2 = torch.zeros((128, 48), dtype=torch.float16, device=device())
     with pytest.raises(pk.PolyKVError):
         pk.polykv_project_compress(x2, w2, w2, pool, lay, 0, 0)     # hidden not a multiple of 64
+
+
+def test_full_size_llama_layer():
+    """One Llama-3-8B layer at 4,096 tokens (hidden 4096, 8 KV heads of 128), the shape the
+    benchmark times: sampled token rows of the plain projection against the oracle, and the
+    whole fused pool against projection + append."""
+    n, hidden, H, d = 4096, 4096, 8, 128
+    print("project full size", flush=True)
+    x, wk, wv = _inputs(n, hidden, H, d, seed=3)
+    lay = pk.polykv_pool_layout(1, H, d, n)
+    xd, wkd, wvd = _dev(x), _dev(wk), _dev(wv)
+    k = torch.empty((H, n, d), dtype=torch.float16, device=device())
+    v = torch.empty_like(k)
+    pk.polykv_project_kv(xd, wkd, wvd, k, v, H, d)
+    fused = new_pool(lay, fill=0x5A)
+    plain = new_pool(lay, fill=0x5A)
+    pk.polykv_project_compress(xd, wkd, wvd, fused, lay, 0, 0)
+    pk.polykv_append_k(k, plain, lay, 0)
+    pk.polykv_append_v(v, plain, lay, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, plain)
+    rows = np.r_[0:8, 1000:1008, 2047:2056, 4088:4096]
+    kg = k.cpu().numpy()[:, rows]
+    vg = v.cpu().numpy()[:, rows]
+    check_projection(kg, x[rows], wk, H, d)
+    check_projection(vg, x[rows], wv, H, d)

@@ -126,3 +126,46 @@ def test_tail_lengths_are_clamped_and_cap_zero_is_a_no_op():
     want = oracle.pool_and_tail_decode(q, kh, vh, tk, tv, np.array([0, cap, 3]), G, scale)
     assert row_rel_err(out.cpu().numpy(), want) <= DECODE_REL_TOL
     assert torch.equal(out[0, 0], before[0, 0])  # the agent with an empty tail is untouched
+
+
+def test_tail_merge_full_size_sampled():
+    """The 4K Llama-3-8B pool (compressed on the GPU) with 15 agents' private tails of up
+    to 128 tokens, in the launch configuration the benchmark times: every layer is merged
+    on the GPU, three layers are checked against the oracle over pool + tail tokens."""
+    from gpu_helpers import C32, layout_for, read_pool, upload_kv
+    from workloads import CONFIGS, gen_q_step
+    cfg = CONFIGS[3]
+    L, H, d, T, A, G, cap = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim, cfg.n_tokens, cfg.n_agents, cfg.gqa, 128
+    _say("tail merge full size", cfg.name)
+    lay = layout_for(cfg)
+    k, v = upload_kv(cfg)
+    pool = torch.zeros(lay.total_bytes, dtype=torch.uint8, device=device())
+    pk.polykv_compress_k(k, pool, lay)
+    pk.polykv_compress_v(v, pool, lay)
+    del k, v
+    lens = [128, 0, 1, 31, 32, 33, 64, 65, 127, 128, 100, 7, 96, 128, 50][:A]
+    rng = np.random.default_rng(2026)
+    tk = rng.standard_normal((A, L, H, cap, d), dtype=np.float32).astype(np.float16)
+    tv = rng.standard_normal((A, L, H, cap, d), dtype=np.float32).astype(np.float16)
+    tl = np.asarray(lens, dtype=np.int32)
+    qn = gen_q_step(cfg, cfg.decode_steps - 1)
+    qd = torch.from_numpy(qn).to(device())
+    out = torch.empty_like(qd)
+    lse = torch.empty((L, A, H * G), dtype=torch.float32, device=device())
+    pk.polykv_attend_shared_lse(pool, lay, qd, out, lse, A, G, cfg.softmax_scale)
+    pk.polykv_attend_tail_merge(lay, qd, out, lse, torch.from_numpy(tk).to(device()),
+                                torch.from_numpy(tv).to(device()), torch.from_numpy(tl).to(device()),
+                                A, G, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    layers = [0, L // 2, L - 1]
+    got = read_pool(pool, lay)
+    tiles = [l * H + h for l in layers for h in range(H)]
+    sub = {"k_codes": got["k_codes"][tiles].reshape(len(layers), H, T, d),
+           "k_scales": got["k_scales"][tiles].reshape(len(layers), H, T, d // 32),
+           "v_planes": got["v_planes"][tiles].reshape(len(layers), H, -1, 3, d),
+           "v_norms": got["v_norms"][tiles].reshape(len(layers), H, T)}
+    kh, vh = oracle.dequant_pool(sub, C32, T)
+    want = oracle.pool_and_tail_decode(qn[layers], kh, vh, tk[:, layers], tv[:, layers], tl, G, cfg.softmax_scale)
+    err = row_rel_err(out.cpu().numpy()[layers], want)
+    _say("  worst row error %.2e" % err)
+    assert err <= DECODE_REL_TOL
