@@ -440,18 +440,39 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
                         const float init = first ? 0.0f : -(m_ref[rb] + kSlack);
                         S[tb][rb] = f4{init, init, init, init};
                     }
+                    // two-stage pipeline over the q8 blocks: block b+1's conversion and its
+                    // hi products are issued before block b's scale FMAs read its results
+                    const uint8_t* kt = st + 16 * D * tb;
+                    h8 ak = codes_to_h8(*reinterpret_cast<const uint2*>(kt + kfrag[0]));
+                    f4 acc[SRB];
+#pragma unroll
+                    for (int rb = 0; rb < SRB; ++rb)
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qh[rb][0], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                    for (int rb = 0; rb < SRB; ++rb)
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, ql[rb][0], acc[rb], 0, 0, 0);
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
-                        const h8 ak = codes_to_h8(*reinterpret_cast<const uint2*>(st + 16 * D * tb + kfrag[b]));
+                        f4 accn[SRB];
+                        h8 akn;
+                        if (b + 1 < NB) {
+                            akn = codes_to_h8(*reinterpret_cast<const uint2*>(kt + kfrag[b + 1]));
 #pragma unroll
-                        for (int rb = 0; rb < SRB; ++rb) {
-                            f4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qh[rb][b], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, ql[rb][b], acc, 0, 0, 0);
+                            for (int rb = 0; rb < SRB; ++rb)
+                                accn[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, qh[rb][b + 1], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int rb = 0; rb < SRB; ++rb)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int si = i * NB + b;
-                                S[tb][rb][i] = __builtin_fmaf(acc[i], (float)scv[si >> 3][si & 7], S[tb][rb][i]);
+                                S[tb][rb][i] = __builtin_fmaf(acc[rb][i], (float)scv[si >> 3][si & 7], S[tb][rb][i]);
                             }
+                        if (b + 1 < NB) {
+#pragma unroll
+                            for (int rb = 0; rb < SRB; ++rb)
+                                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, ql[rb][b + 1], accn[rb], 0, 0, 0);
+                            ak = akn;
                         }
                     }
                 }
