@@ -32,10 +32,17 @@
 #include <hip/hip_fp16.h>
 
 
+#include "lds_dma.h"
 #include "polykv_internal.h"
 
 namespace polykv {
 namespace {
+
+using lds_dma::dma16;
+using lds_dma::dma4;
+using lds_dma::lane_id;
+using lds_dma::lds_addr;
+using lds_dma::wait_vm;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -111,22 +118,6 @@ struct MCfg {
     static_assert(SLOTS <= 16 && 1024 % D == 0, "the key swizzle repeats every 1 KB");
 };
 
-// ---- direct-to-LDS DMA through inline asm: the compiler does not track these loads, so
-// it inserts no vmcnt(0) before LDS reads; each wave waits on its own loads with explicit
-// vmcnt counts. Address = 64-bit scalar base + 32-bit per-lane offset; LDS destination =
-// M0 + 16 * lane (4 * lane for dwords).
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-                 :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
 // wait until at most n (0..3) later chunks of LOADS instructions each are still in flight
 template <int LOADS>
 __device__ __forceinline__ void wait_chunks_after(int n) {
@@ -136,7 +127,6 @@ __device__ __forceinline__ void wait_chunks_after(int n) {
     else wait_vm<0>();
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // 8 int8 codes -> 8 fp16 (exact): sign-extending byte selects, two results per dword.
 // One asm block, because the compiler's hazard tracking does not look inside inline asm:
@@ -201,13 +191,6 @@ struct TileSrc {
 // every 1 KB, so instruction i reads koff + 1 KB * i. In the tile's last, partial chunk,
 // rows past the end of the tile are clamped to the last token (valid memory; those
 // tokens get weight 0 in the softmax).
-// lane id, recomputed at every use: volatile so that the compiler neither hoists it (and
-// the offsets derived from it) out of the loop nor keeps it live across the loop
-__device__ __forceinline__ uint32_t lane_id() {
-    uint32_t r;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
-    return r;
-}
 
 // The lane offsets are derived from the lane id where they are used, so that nothing
 // stays live across the score loop for them.

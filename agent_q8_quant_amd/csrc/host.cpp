@@ -277,7 +277,8 @@ int polykv_append_v(const void* v_fp16, void* pool, const polykv_layout_t* layou
 }
 
 static int check_projection(int32_t n_tok, int32_t hidden, int32_t n_heads, int32_t head_dim) {
-    if (n_tok < 1 || n_heads < 1 || hidden < 64 || hidden % 64 != 0) return POLYKV_ERR_SHAPE;
+    // hidden <= 2^22 keeps every per-lane byte offset of a 256-row operand tile in 32 bits
+    if (n_tok < 1 || n_heads < 1 || hidden < 64 || hidden % 64 != 0 || hidden > (1 << 22)) return POLYKV_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return POLYKV_ERR_SHAPE;
     return POLYKV_OK;
 }

@@ -9,20 +9,22 @@
 // polykv_append_k/v. The same kernel without the compression (mode STORE) writes the fp16
 // projection, head-major [H][n_tok][d], for that unfused path.
 //
-// Work layout: one workgroup per (128-token tile, head, K or V), four waves; wave w owns
-// tokens 32 w .. 32 w + 31 of the tile and all d columns of the head. The reduction over
-// the hidden size runs in 64-wide steps: both operand tiles ([128 tokens][64] of x and
-// [d outputs][64] of W, k-contiguous, 16-byte pieces XOR-swizzled by row) go through two
-// LDS stages, and every thread holds the pieces of the step after next in registers while
-// the current step is multiplied (v_mfma_f32_32x32x16_f16: 32 tokens x 32 outputs per instruction, fp16
-// operands, fp32 accumulation). After the last step each wave rounds its 32 x d block to
-// fp16 into LDS and encodes it: keys with the q8_0 codec (one lane per 8 entries), values
-// with the matrix-core TurboQuant codec (the wave's 32 tokens are one 32-token group).
+// Work layout: one workgroup per (256-token tile, head, K or V), eight waves. The reduction
+// over the hidden size runs in 64-wide steps: both operand tiles ([256 tokens][64] of x and
+// [d outputs][64] of W, k-contiguous, 16-byte pieces XOR-swizzled by row) stream into a
+// three-deep LDS ring by direct-to-LDS loads issued two steps ahead, one barrier per step.
+// Wave w multiplies a 64-token x 64-output block (32-token x 64-output for d = 64) with
+// v_mfma_f32_32x32x16_f16 (fp16 operands, fp32 accumulation), two by two 32 x 32 tiles, so
+// every operand fragment read from LDS feeds two products. After the last step the
+// workgroup rounds its 256 x d block to fp16 into LDS, and wave w encodes tokens
+// 32 w .. 32 w + 31: keys with the q8_0 codec (one lane per 8 entries), values with the
+// matrix-core TurboQuant codec (the wave's 32 tokens are one 32-token group).
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
 #include "codec.h"
+#include "lds_dma.h"
 #include "polykv_internal.h"
 
 namespace polykv {
@@ -32,27 +34,44 @@ using codec::h8;
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;   // tokens per workgroup
-constexpr int BK = 64;    // hidden entries per step
+constexpr int BM = 256;     // tokens per workgroup
+constexpr int BK = 64;      // hidden entries per step
+constexpr int NST = 3;      // LDS ring depth (steps)
+static_assert(NST == 3, "the ring waits assume loads two steps ahead");
+#ifndef PJ_WAVES
+#define PJ_WAVES 8
+#endif
+#ifndef PJ_WN128
+#define PJ_WN128 2
+#endif
 
 template <int D>
 struct PjCfg {
-    static constexpr int NT = D / 32;                 // 32-column output tiles per wave
-    static constexpr int X_PIECES = BM * BK / 8;      // 16-byte pieces of the x tile
-    static constexpr int W_PIECES = D * BK / 8;
-    static constexpr int XPT = X_PIECES / 256;        // per thread
-    static constexpr int WPT = W_PIECES / 256;
-    static constexpr int OFF_X = 0;                                  // two stages of x and W
-    static constexpr int OFF_W = OFF_X + BM * BK * 2;
-    static constexpr int STAGE_BYTES = OFF_W + D * BK * 2;
-    static constexpr int LDS_MAIN = 2 * STAGE_BYTES;
-    static constexpr int STAGE = 32 * D * 2;          // one wave's fp16 block (epilogue)
-    static constexpr int LDS = LDS_MAIN > 4 * STAGE ? LDS_MAIN : 4 * STAGE;
-    static_assert(XPT >= 1 && WPT >= 1, "whole pieces per thread");
+    static constexpr int WAVES = PJ_WAVES;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int WN = D == 128 ? PJ_WN128 : 1; // waves across the outputs
+    static constexpr int WM = WAVES / WN;             // waves across the tokens
+    static constexpr int MT = BM / WM / 32;           // 32-token tiles per wave
+    static constexpr int NT = D / 32 / WN;            // 32-output tiles per wave
+    static constexpr int X_BYTES = BM * BK * 2;       // one step of x
+    static constexpr int W_BYTES = D * BK * 2;        // one step of W
+    static constexpr int X_INSTR = X_BYTES / 1024 / WAVES;   // DMA instructions per wave and step
+    static constexpr int W_INSTR = W_BYTES / 1024 / WAVES;
+    static constexpr int LOADS = X_INSTR + W_INSTR;
+    static constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
+    static constexpr int LDS_MAIN = NST * STAGE_BYTES;
+    static constexpr int LDS_OUT = BM * D * 2;        // the fp16 block (epilogue)
+    static constexpr int LDS = LDS_MAIN > LDS_OUT ? LDS_MAIN : LDS_OUT;
+    static_assert(WM * WN == WAVES && MT >= 1 && NT >= 1 && 32 * NT * WN == D, "wave grid");
+    static_assert(X_INSTR * WAVES * 1024 == X_BYTES && W_INSTR * WAVES * 1024 == W_BYTES, "whole DMA instructions");
+    static_assert((NST - 1) * LOADS <= 63 && LDS <= 160 * 1024, "vmcnt and LDS budgets");
+    static_assert(STAGE_BYTES % 256 == 0 && X_BYTES % 256 == 0, "256-byte aligned DMA destinations");
 };
 
-// LDS offset (bytes) of the 16-byte piece c (0..7) of row r of a [rows][64] fp16 tile
-__device__ __forceinline__ uint32_t sw_off(uint32_t r, uint32_t c) { return r * 128u + ((c ^ (r & 7u)) << 4); }
+// LDS offset (bytes) of the 16-byte piece c (0..7) of row r of a [rows][64] fp16 tile. The
+// XOR with bits 1..3 of the row puts the 16 rows one fragment read touches (same piece) on
+// 16 distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t sw_off(uint32_t r, uint32_t c) { return r * 128u + ((c ^ ((r >> 1) & 7u)) << 4); }
 
 struct PjArgs {
     const __half* x;        // [n_tok][hidden]
@@ -66,97 +85,37 @@ struct PjArgs {
 
 enum { MODE_STORE = 0, MODE_POOL = 1 };
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void k_project(PjArgs a) {
-    using C = PjCfg<D>;
-    constexpr int NT = C::NT;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t_tile = blockIdx.x * BM;                    // first token of the tile (chunk-relative)
-    const int h = blockIdx.y;
-    const int which = blockIdx.z;                          // 0: K, 1: V
-    const int n_tok = a.n_tok, hidden = a.hidden;
-    const __half* wmat = a.w[which] + (size_t)h * D * hidden;
-
-    // global -> register pieces of step k0: piece p of x is row p / 8, column piece p % 8;
-    // rows past the chunk read its last row (valid memory; their results are not stored)
-    u4 px[C::XPT], pw[C::WPT];
-    auto fetch = [&](int k0) {
+// One step's operand tiles into ring stage `st` by direct-to-LDS loads. Destination piece P
+// (16 bytes, lane-linear within each 1 KB instruction) is row P / 8, slot P % 8 of its
+// tile; it holds global piece (P % 8) ^ ((row >> 1) & 7) of that row, which realises the
+// swizzle of sw_off. Rows past the chunk read its last row (valid memory; their results
+// are not stored).
+template <class C>
+__device__ __forceinline__ void issue_step(const __half* xt, const __half* wmat, int hidden, int k0,
+                                           int rows_valid, int w, uint8_t* stage) {
+    const uint32_t lane = lds_dma::lane_id();
+    const uint32_t row_bytes = (uint32_t)hidden * 2u;
 #pragma unroll
-        for (int i = 0; i < C::XPT; ++i) {
-            const int p = tid + 256 * i, r = p >> 3, c = p & 7;
-            const int row = min(t_tile + r, n_tok - 1);
-            px[i] = *reinterpret_cast<const u4*>(a.x + (size_t)row * hidden + k0 + 8 * c);
-        }
-#pragma unroll
-        for (int i = 0; i < C::WPT; ++i) {
-            const int p = tid + 256 * i, r = p >> 3, c = p & 7;
-            pw[i] = *reinterpret_cast<const u4*>(wmat + (size_t)r * hidden + k0 + 8 * c);
-        }
-    };
-
-    f16v acc[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = f16v{};
-
-    // two LDS stages: step ks multiplies stage ks % 2 while the registers of step ks + 1 go
-    // into the other stage and the loads of step ks + 2 are in flight; one barrier per step
-    const int steps = hidden / BK;
-    auto put = [&](int st) {
-        uint8_t* base = lds + st * C::STAGE_BYTES;
-#pragma unroll
-        for (int i = 0; i < C::XPT; ++i) {
-            const int p = tid + 256 * i;
-            *reinterpret_cast<u4*>(base + C::OFF_X + sw_off(p >> 3, p & 7)) = px[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::WPT; ++i) {
-            const int p = tid + 256 * i;
-            *reinterpret_cast<u4*>(base + C::OFF_W + sw_off(p >> 3, p & 7)) = pw[i];
-        }
-    };
-    fetch(0);
-    put(0);
-    if (steps > 1) fetch(BK);
-    __syncthreads();
-    for (int ks = 0; ks < steps; ++ks) {
-        const uint8_t* base = lds + (ks & 1) * C::STAGE_BYTES;
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            // lane l: row l % 32 of its block, k = 16 s + 8 (l / 32) .. + 7 (piece 2 s + l / 32)
-            const uint32_t c = 2u * s + (uint32_t)(lane >> 5);
-            const h8 av = *reinterpret_cast<const h8*>(base + C::OFF_X + sw_off(32u * w + (lane & 31), c));
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const h8 bv = *reinterpret_cast<const h8*>(base + C::OFF_W + sw_off(32u * j + (lane & 31), c));
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[j], 0, 0, 0);
-            }
-        }
-        if (ks + 1 < steps) {
-            put((ks + 1) & 1);                          // its readers finished before the last barrier
-            if (ks + 2 < steps) fetch((ks + 2) * BK);
-        }
-        __syncthreads();
+    for (int i = 0; i < C::X_INSTR; ++i) {
+        const int q = w + C::WAVES * i;                    // instruction index within the x tile
+        const uint32_t P = 64u * (uint32_t)q + lane, r = P >> 3, c = (P & 7u) ^ ((r >> 1) & 7u);
+        const uint32_t rr = min(r, (uint32_t)rows_valid - 1u);
+        lds_dma::dma16(xt + k0, rr * row_bytes + 16u * c, lds_dma::lds_addr(stage + 1024 * q));
     }
-
-    // ---- epilogue: the wave's 32 x D block, rounded to fp16, into its LDS stage (the
-    // loop's last barrier: every wave is done with the operand tiles) ----
-    __half* stage = reinterpret_cast<__half*>(lds + w * C::STAGE);   // [32 tokens][D]
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            // register i: token 8 (i / 4) + 4 (l / 32) + i % 4, output column l % 32 of tile j
-            const int m = 8 * (i / 4) + 4 * (lane >> 5) + (i & 3);
-            stage[m * D + 32 * j + (lane & 31)] = __float2half_rn(acc[j][i]);
-        }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = 0; i < C::W_INSTR; ++i) {
+        const int q = w + C::WAVES * i;
+        const uint32_t P = 64u * (uint32_t)q + lane, r = P >> 3, c = (P & 7u) ^ ((r >> 1) & 7u);
+        lds_dma::dma16(wmat + k0, r * row_bytes + 16u * c, lds_dma::lds_addr(stage + C::X_BYTES + 1024 * q));
+    }
+}
 
-    const int t_wave = t_tile + 32 * w;                    // chunk-relative first token
-    if (t_wave >= n_tok) return;                           // wave-uniform
+// One 32-token group of the projected block (fp16 in LDS, [32 tokens][D]): written as fp16
+// (mode STORE) or encoded into the pool.
+template <int D, int MODE>
+__device__ __forceinline__ void encode_group(const PjArgs& a, const __half* stage, int t_wave, int which,
+                                             int h, int lane) {
+    const int n_tok = a.n_tok;
     constexpr int PPR = D / 8;                             // 16-byte pieces per token row
     if constexpr (MODE == MODE_STORE) {
         __half* out = a.out[which] + (size_t)h * n_tok * D;
@@ -166,7 +125,6 @@ __global__ __launch_bounds__(256) void k_project(PjArgs a) {
                 *reinterpret_cast<u4*>(out + (size_t)(t_wave + m) * D + 8 * c) =
                     *reinterpret_cast<const u4*>(stage + m * D + 8 * c);
         }
-        return;
     } else {
         const PoolGeom& g = a.g;
         const size_t tile = (size_t)a.layer * g.n_kv_heads + h;
@@ -213,13 +171,95 @@ __global__ __launch_bounds__(256) void k_project(PjArgs a) {
 }
 
 template <int D, int MODE>
+__global__ __launch_bounds__(PjCfg<D>::THREADS, 1) void k_project(PjArgs a) {
+    using C = PjCfg<D>;
+    constexpr int MT = C::MT, NT = C::NT;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t_tile = blockIdx.x * BM;                    // first token of the tile (chunk-relative)
+    const int h = blockIdx.y;
+    const int which = blockIdx.z;                          // 0: K, 1: V
+    const int n_tok = a.n_tok, hidden = a.hidden;
+    const __half* wmat = a.w[which] + (size_t)h * D * hidden;
+    const __half* xt = a.x + (size_t)t_tile * hidden;
+    const int rows_valid = min(BM, n_tok - t_tile);
+    const int wm = w / C::WN, wn = w - wm * C::WN;
+    const uint32_t row0 = 32u * MT * wm, col0 = 32u * NT * wn;  // the wave's block in the tile
+
+    f16v acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f16v{};
+
+    // ring of NST stages: step ks multiplies stage ks % NST; the loads of step ks + NST - 1
+    // go into the stage step ks - 1 used, after the barrier that ends every wave's reads of it
+    const int steps = hidden / BK;
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < steps) issue_step<C>(xt, wmat, hidden, s * BK, rows_valid, w, lds + s * C::STAGE_BYTES);
+    for (int ks = 0; ks < steps; ++ks) {
+        // this step's loads (and those of every earlier step) have landed, in every wave:
+        // only the next step's may still be in flight
+        if (ks + 1 < steps) lds_dma::wait_vm<C::LOADS>();
+        else lds_dma::wait_vm<0>();
+        __syncthreads();
+        if (ks + NST - 1 < steps)
+            issue_step<C>(xt, wmat, hidden, (ks + NST - 1) * BK, rows_valid, w,
+                          lds + ((ks + NST - 1) % NST) * C::STAGE_BYTES);
+        const uint8_t* xs = lds + (ks % NST) * C::STAGE_BYTES;
+        const uint8_t* ws = xs + C::X_BYTES;
+#pragma unroll
+        for (int ss = 0; ss < BK / 16; ++ss) {
+            // lane l: row l % 32 of a tile, k = 16 ss + 8 (l / 32) .. + 7 (piece 2 ss + l / 32)
+            const uint32_t c = 2u * ss + (uint32_t)(lane >> 5);
+            h8 av[MT], bv[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                av[i] = *reinterpret_cast<const h8*>(xs + sw_off(row0 + 32u * i + (lane & 31), c));
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                bv[j] = *reinterpret_cast<const h8*>(ws + sw_off(col0 + 32u * j + (lane & 31), c));
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // every wave is done with the ring: the fp16 block reuses it
+
+    // the workgroup's BM x D block, rounded to fp16, into LDS [BM tokens][D]
+    __half* blk = reinterpret_cast<__half*>(lds);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                // register e: token 8 (e / 4) + 4 (l / 32) + e % 4, output column l % 32 of the tile
+                const uint32_t m = row0 + 32u * i + 8u * (e / 4) + 4u * (lane >> 5) + (e & 3);
+                blk[m * D + col0 + 32u * j + (lane & 31)] = __float2half_rn(acc[i][j][e]);
+            }
+    __syncthreads();
+
+    // ---- epilogue: the tile's 32-token groups, wave w taking groups w, w + WAVES, ... ----
+    for (int grp32 = w; grp32 < BM / 32; grp32 += C::WAVES) {
+        const int t_wave = t_tile + 32 * grp32;            // chunk-relative first token
+        if (t_wave >= n_tok) break;                        // wave-uniform
+        encode_group<D, MODE>(a, blk + 32 * grp32 * D, t_wave, which, h, lane);
+    }
+}
+
+template <int D, int MODE>
 hipError_t launch_t(const PjArgs& a, int nz, hipStream_t s) {
     using C = PjCfg<D>;
     auto kern = k_project<D, MODE>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     dim3 grid((a.n_tok + BM - 1) / BM, a.n_heads, nz);
-    hipLaunchKernelGGL(kern, grid, dim3(256), C::LDS, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(C::THREADS), C::LDS, s, a);
     return hipGetLastError();
 }
 
