@@ -5,8 +5,9 @@ compression of the fp16 K and V of every layer into the pool (compress_k + compr
 then D decode steps of all agents against that pool (one attend_shared launch each).
 Inputs (fp16 K/V and the queries of all D decode steps) are resident in HBM before timing.
 
-Every launch goes to one explicit stream and is bracketed by HIP events recorded on that
-stream. Three identical copies of the pool are used in turn, so each decode launch reads a
+Every launch goes to one explicit stream; HIP events recorded on that stream bracket each
+compress launch and each step's run of D back-to-back decode launches (average decode
+launch = that interval / D). Three identical copies of the pool are used in turn, so each decode launch reads a
 copy that at least two pool-sized streams have passed through the 256 MB Infinity Cache
 since it was last touched: it comes from HBM (--warm uses a single copy). Decode launches
 right after a 1 GiB write (cold caches and address translations) are timed separately and
@@ -210,9 +211,11 @@ def main():
         e.append(ev())
         pk.polykv_compress_v(v, pools[pw], lay, stream=stream)
         e.append(ev())
+        # the D decode launches back to back, one event pair around them: an event between
+        # launches would add its own packet's time to every launch
         for s in range(D):
             decode((pw + 1 + s) % n_pools, s)
-            e.append(ev())
+        e.append(ev())
         rec.append(e)
 
     def append_all(i):
@@ -357,7 +360,7 @@ def main():
     step_ms = [r[0].elapsed_time(r[-1]) for r in rec]
     ck_ms = [r[0].elapsed_time(r[1]) for r in rec]
     cv_ms = [r[1].elapsed_time(r[2]) for r in rec]
-    at_ms = [r[i].elapsed_time(r[i + 1]) for r in rec for i in range(2, 2 + D)]
+    at_ms = [r[2].elapsed_time(r[3]) / D for r in rec]
     step_s = sum(step_ms) / len(step_ms) / 1e3
     t_ck = sum(ck_ms) / len(ck_ms) / 1e3
     t_cv = sum(cv_ms) / len(cv_ms) / 1e3
