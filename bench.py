@@ -357,6 +357,20 @@ def main():
                     dq_ev[which].append((e0, e1))
         stream.synchronize()
 
+        # Achievable-bandwidth reference: a plain device copy of one pool copy into another
+        # buffer (read + write of the pool's bytes), the source rotating like the decode's
+        cp_dst = torch.empty_like(pools[0])
+        cp_ev = []
+        with torch.cuda.stream(stream):
+            for i in range(n_pools + 12):
+                e0 = ev()
+                cp_dst.copy_(pools[i % n_pools])
+                e1 = ev()
+                if i >= n_pools:
+                    cp_ev.append((e0, e1))
+        stream.synchronize()
+        del cp_dst
+
     step_ms = [r[0].elapsed_time(r[-1]) for r in rec]
     ck_ms = [r[0].elapsed_time(r[1]) for r in rec]
     cv_ms = [r[1].elapsed_time(r[2]) for r in rec]
@@ -448,6 +462,11 @@ def main():
         "algorithmic_bytes_per_launch": {"k": dk_bytes, "v": dv_bytes},
         "traffic": {"k": _traffic("dequant_k", ["dequant.hip"], workload),
                     "v": _traffic("dequant_v", ["dequant.hip"], workload)}}
+    t_cp = sum(a.elapsed_time(b) for a, b in cp_ev) / len(cp_ev) / 1e3
+    result["device_copy_reference"] = {
+        "what": "torch copy of one pool copy (read + write), sources rotating like the decode",
+        "bytes": 2 * lay.total_bytes, "us": t_cp * 1e6, "GBps": 2 * lay.total_bytes / t_cp / 1e9,
+        "frac_hbm": 2 * lay.total_bytes / t_cp / 1e9 / HBM_PEAK_GBPS}
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         n = args.cpu_sample_layers or cfg.n_layers
