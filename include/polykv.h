@@ -169,7 +169,7 @@ int polykv_append_v(const void* v_fp16, void* pool, const polykv_layout_t* layou
  *  pool:     device, layout->total_bytes, 256-B aligned; layer `layer`, tokens
  *            [token_begin, token_begin + n_tok) are written (token_begin a multiple of 32;
  *            plane bits of later tokens below the capacity in the last group are kept).
- *  hidden:   a multiple of 64; head_dim 64 or 128.
+ *  hidden:   a multiple of 64, at most 2^22; head_dim 64 or 128.
  * Errors: NULL, SHAPE, ALIGN, RANGE (layer, token range, token_begin % 32), LAYOUT,
  *         CODEBOOK, DEVICE, LAUNCH.
  */

@@ -229,6 +229,7 @@ def test_projection_validation(L):
     assert fused(x=None) == -1
     assert fused(wv=None) == -1
     assert fused(hidden=96) == -2          # not a multiple of 64
+    assert fused(hidden=(1 << 22) + 64) == -2  # operand-tile byte offsets must fit 32 bits
     assert fused(n=0) == -2
     assert fused(x=ctypes.c_void_p(0x10008)) == -3
     assert fused(pool=ctypes.c_void_p(0x20010)) == -3
@@ -242,6 +243,7 @@ def test_projection_validation(L):
     assert plain(wv=A16, v=None) == -1     # V output missing
     assert plain(hd=32) == -2
     assert plain(heads=0) == -2
+    assert plain(hidden=1 << 23) == -2
     assert plain(k=ctypes.c_void_p(0x10004)) == -3
 
 
