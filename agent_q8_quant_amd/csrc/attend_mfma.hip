@@ -59,8 +59,10 @@ constexpr float kSlack = 8.0f;  // log2 units a score may exceed the reference m
 
 constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// D: head_dim; SRB: 16-row blocks per score wave; NSW: score waves per stream.
-template <int D, int SRB, int NSW>
+// D: head_dim; SRB: 16-row blocks per score wave; NSW: score waves per stream; LUT: value
+// decode through the 4096-entry table (else through the 64-entry pair table, which keeps
+// the LDS small enough for two workgroups per CU).
+template <int D, int SRB, int NSW, bool LUT>
 struct MCfg {
     static constexpr int NB = D / 32;                  // q8 blocks per row
     static constexpr int NRB = SRB * NSW;              // 16-row blocks per tile
@@ -95,7 +97,7 @@ struct MCfg {
     static constexpr int ST_OFF_P = ST_OFF_B + NSV * B_STAGE;
     static constexpr int ST_OFF_AL = ST_OFF_P + 2 * P_BYTES;
     static constexpr int STREAM_BYTES = round_up(ST_OFF_AL + 2 * AL_STRIDE * 4, 256);
-    static constexpr int LUT_BYTES = 4096 * 8;
+    static constexpr int LUT_BYTES = LUT ? 4096 * 8 : 0;
     static constexpr int OFF_LUT = 0;
     static constexpr int OFF_MASK = LUT_BYTES;                 // fp16 [2][CHUNK] token weights
     static constexpr int OFF_PAIR = OFF_MASK + 256;            // fp16 [64][2] pair table
@@ -251,9 +253,9 @@ __device__ __forceinline__ void issue_planes(const TileSrc& ts, int c, int half,
     }
 }
 
-template <int D, int SRB, int NSW>
+template <int D, int SRB, int NSW, bool LUT>
 __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(AttendArgs a) {
-    using C = MCfg<D, SRB, NSW>;
+    using C = MCfg<D, SRB, NSW, LUT>;
     constexpr int NB = C::NB, NRB = C::NRB, ROWS = C::ROWS, VDB = C::VDB, HD = C::HD;
     constexpr int AL_STRIDE = C::AL_STRIDE;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
             (!tail || (NC - 1) * CHUNK + t < T) ? (_Float16)1.0f : (_Float16)0.0f;
     }
     __syncthreads();  // pair table complete
-    {
+    if constexpr (LUT) {
         const uint32_t* pair = reinterpret_cast<const uint32_t*>(lds + C::OFF_PAIR);
         uint2* lut = reinterpret_cast<uint2*>(lds + C::OFF_LUT);
         for (int e = tid; e < 4096; e += C::THREADS) {
@@ -535,6 +537,7 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
         // ===================== value waves =====================
         const int half = role - NSW;
         const h4* lut = reinterpret_cast<const h4*>(lds + C::OFF_LUT);
+        const h2* pairs = reinterpret_cast<const h2*>(lds + C::OFF_PAIR);
         const uint32_t sh = 4u * (uint32_t)j;
         for (int k = 0; k <= nk_max; ++k) {
             const int kk = k - 1;  // one chunk behind the score waves
@@ -579,13 +582,26 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
 #pragma unroll
                 for (int db = 0; db < VDB; ++db) {
                     const uint32_t w0 = wv[0][db], w1 = wv[1][db], w2 = wv[2][db];
-                    const uint32_t ilo = __builtin_amdgcn_ubfe(w0, sh, 4) | (__builtin_amdgcn_ubfe(w1, sh, 4) << 4) |
-                                         (__builtin_amdgcn_ubfe(w2, sh, 4) << 8);
-                    const uint32_t ihi = __builtin_amdgcn_ubfe(w0, sh + 16u, 4) |
-                                         (__builtin_amdgcn_ubfe(w1, sh + 16u, 4) << 4) |
-                                         (__builtin_amdgcn_ubfe(w2, sh + 16u, 4) << 8);
-                    const h4 vlo = lut[ilo], vhi = lut[ihi];
-                    const h8 bv = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+                    h8 bv;
+                    if constexpr (LUT) {
+                        // tokens 4j .. 4j + 3 and 16 + 4j .. + 3: one table entry each
+                        const uint32_t ilo = __builtin_amdgcn_ubfe(w0, sh, 4) | (__builtin_amdgcn_ubfe(w1, sh, 4) << 4) |
+                                             (__builtin_amdgcn_ubfe(w2, sh, 4) << 8);
+                        const uint32_t ihi = __builtin_amdgcn_ubfe(w0, sh + 16u, 4) |
+                                             (__builtin_amdgcn_ubfe(w1, sh + 16u, 4) << 4) |
+                                             (__builtin_amdgcn_ubfe(w2, sh + 16u, 4) << 8);
+                        const h4 vlo = lut[ilo], vhi = lut[ihi];
+                        bv = h8{vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+                    } else {
+                        // the same tokens two at a time through the pair table
+                        auto pidx = [&](uint32_t b) {
+                            return __builtin_amdgcn_ubfe(w0, b, 2) | (__builtin_amdgcn_ubfe(w1, b, 2) << 2) |
+                                   (__builtin_amdgcn_ubfe(w2, b, 2) << 4);
+                        };
+                        const h2 p0 = pairs[pidx(sh)], p1 = pairs[pidx(sh + 2u)];
+                        const h2 p2 = pairs[pidx(sh + 16u)], p3 = pairs[pidx(sh + 18u)];
+                        bv = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                    }
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb)
                         O[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[rb], bv, O[rb][db], 0, 0, 0);
@@ -700,10 +716,10 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
     }
 }
 
-template <int D, int SRB, int NSW>
+template <int D, int SRB, int NSW, bool LUT = true>
 hipError_t launch_t(const AttendArgs& a, hipStream_t s) {
-    using C = MCfg<D, SRB, NSW>;
-    auto kern = k_attend_mfma<D, SRB, NSW>;
+    using C = MCfg<D, SRB, NSW, LUT>;
+    auto kern = k_attend_mfma<D, SRB, NSW, LUT>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
     const uint32_t tiles = (uint32_t)a.layer_count * (uint32_t)a.g.n_kv_heads;
@@ -726,7 +742,8 @@ hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
         return launch_t<128, 2, 2>(a, s);
     }
     if (a.g.head_dim == 64) {
-        if (nrb == 1) return launch_t<64, 1, 1>(a, s);
+        // up to 16 rows at d = 64 the workgroup fits 2 per CU without the big table
+        if (nrb == 1) return launch_t<64, 1, 1, false>(a, s);
         if (nrb == 2) return launch_t<64, 1, 2>(a, s);
         return launch_t<64, 2, 2>(a, s);
     }
