@@ -17,12 +17,15 @@
 //   precision), applies the block scales with v_fma_mix, runs a lazy-max online softmax
 //   in base 2 and writes p * n_t as fp16 to a double-buffered LDS slot. A value wave owns
 //   half of the head dimensions: it decodes the value bit-planes of its dimensions to
-//   fp16 centroids through a 4096-entry table (one nibble of each plane = 4 tokens) and
-//   accumulates P.V for every row in fp32, one chunk behind the score waves. Four waves
-//   of similar register size per SIMD hide each other's latencies;
+//   fp16 centroids through a 4096-entry table (one nibble of each plane = 4 tokens; for
+//   small workgroups, through the 64-entry pair table it is built from, two tokens per
+//   lookup, so that two workgroups fit one CU) and accumulates P.V for every row in fp32,
+//   one chunk behind the score waves. Four waves of similar register size per SIMD hide
+//   each other's latencies;
 // - the first score wave of a stream streams the keys, block scales and norms of its
 //   chunks into a four-deep LDS ring by direct-to-LDS DMA (256-byte aligned
-//   destinations); each value wave streams its half of the planes into a three-deep ring. One workgroup barrier per chunk step publishes keys and probabilities;
+//   destinations); each value wave streams its half of the planes into a three-deep
+//   ring. One workgroup barrier per chunk step publishes keys and probabilities;
 // - a row's reference maximum is raised only when a score exceeds it by more than 8
 //   (log2 units); the score wave then passes per-row rescale factors to the value waves;
 // - at the end the streams' (m, l, acc) are merged through LDS and each row becomes

@@ -38,18 +38,11 @@ constexpr int BM = 256;     // tokens per workgroup
 constexpr int BK = 64;      // hidden entries per step
 constexpr int NST = 3;      // LDS ring depth (steps)
 static_assert(NST == 3, "the ring waits assume loads two steps ahead");
-#ifndef PJ_WAVES
-#define PJ_WAVES 8
-#endif
-#ifndef PJ_WN128
-#define PJ_WN128 2
-#endif
-
 template <int D>
 struct PjCfg {
-    static constexpr int WAVES = PJ_WAVES;
+    static constexpr int WAVES = 8;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int WN = D == 128 ? PJ_WN128 : 1; // waves across the outputs
+    static constexpr int WN = D / 64;                 // waves across the outputs
     static constexpr int WM = WAVES / WN;             // waves across the tokens
     static constexpr int MT = BM / WM / 32;           // 32-token tiles per wave
     static constexpr int NT = D / 32 / WN;            // 32-output tiles per wave
