@@ -111,10 +111,17 @@ struct MCfg {
     static constexpr int S_LANES = S_BYTES / 4;
     static constexpr int A_LOADS = K_INSTR + 2;
     // merge area (reuses the stream areas at the end)
-    static constexpr int MERGE_BYTES = (2 * STREAMS * ROWS + 2 * ROWS * D) * 4;
+    // merge area: m and l per stream and row, then two partial accumulators of ROWS rows;
+    // a row takes MRS floats and each 32-dim quarter of it MQS, so that 16-byte accesses
+    // of consecutive lanes (4 dims of rows 4 apart, or quarters of neighbouring rows)
+    // fall into distinct LDS banks
+    static constexpr int MQS = 36;
+    static constexpr int MRS = round_up(NB * MQS, 32) + 16;
+    static constexpr int MERGE_BYTES = (2 * STREAMS * ROWS + 2 * ROWS * MRS) * 4;
     static_assert(K_BYTES % 1024 == 0, "key stage is whole DMA instructions");
     static_assert(S_LANES <= 64 && V_LANES <= 64, "one DMA instruction each");
     static_assert(MERGE_BYTES <= STREAMS * STREAM_BYTES, "merge area fits");
+    static_assert(MQS % 4 == 0 && MRS % 4 == 0 && (2 * STREAMS * ROWS) % 4 == 0, "16-byte merge accesses");
     static_assert(LDS <= 160 * 1024, "fits the LDS of one CU");
     static_assert(NSK <= 4 && NSV <= 4 && 3 * A_LOADS <= 63, "wait_chunks_after covers the rings");
     static_assert(S_BYTES <= 256 && N_BYTES <= 256 && K_BYTES % 256 == 0 && OFF_STREAMS % 256 == 0,
@@ -295,41 +302,40 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
     float* albuf = reinterpret_cast<float*>(sbase + C::ST_OFF_AL);  // [2][AL_STRIDE]
     const size_t HG = (size_t)H * G;
 
+    // The start-up latencies overlap: the first DMA chunks, then the query loads, are in
+    // flight while the lookup tables are built; the queries are converted afterwards.
+    // start streaming NSK - 1 key chunks and NSV - 1 plane chunks ahead
+    const bool key_wave = score_wave && role == 0;
+    if (key_wave) {
+        for (int s = 0; s < NSK - 1; ++s)
+            if (s < nk) issue_keys_any<C>(ts, stream + STREAMS * s, kring + s * C::K_BYTES, mring + s * C::M_STAGE);
+    } else if (!score_wave) {
+        for (int s = 0; s < NSV - 1; ++s)
+            if (s < nk) issue_planes<C>(ts, stream + STREAMS * s, role - NSW, bring + s * C::B_STAGE);
+    }
+
     // ---- score waves: queries (B operand). Lane holds row 16 rb + l16 of its row
-    // blocks, dims 32b + 8j .. +7, times scale * log2(e), as fp16 hi + lo. Loaded before
-    // any DMA is issued so that the compiler's own vmcnt waits do not wait on the DMA.
+    // blocks, dims 32b + 8j .. +7, times scale * log2(e), as fp16 hi + lo.
     h8 qh[SRB][NB], ql[SRB][NB];
     float m_ref[SRB], l_run[SRB];
+    float4 qraw[SRB][NB][2];
     if (score_wave) {
-        const float qs = a.softmax_scale * kLog2e;
 #pragma unroll
         for (int rb = 0; rb < SRB; ++rb) {
             m_ref[rb] = -INFINITY;
             l_run[rb] = 0.0f;
             const int r = 16 * (SRB * role + rb) + l16;
-            const float* qrow = nullptr;
             if (r < R) {
                 const int ag = r / G, jj = r - ag * G;
-                qrow = a.q + (((size_t)l_local * A + ag) * HG + (size_t)h * G + jj) * D;
-            }
+                const float* qrow = a.q + (((size_t)l_local * A + ag) * HG + (size_t)h * G + jj) * D;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                float x[8];
-                if (qrow) {
-                    const float4 u0 = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * j);
-                    const float4 u1 = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * j + 4);
-                    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-                    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+                for (int b = 0; b < NB; ++b) {
+                    qraw[rb][b][0] = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * j);
+                    qraw[rb][b][1] = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * j + 4);
                 }
+            } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] *= qs;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qh[rb][b][e] = (_Float16)x[e];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ql[rb][b][e] = (_Float16)(x[e] - (float)qh[rb][b][e]);
+                for (int b = 0; b < NB; ++b) qraw[rb][b][0] = qraw[rb][b][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         }
     }
@@ -362,17 +368,24 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
             lut[e] = make_uint2(pair[i01], pair[i23]);
         }
     }
-    // start streaming NSK - 1 key chunks and NSV - 1 plane chunks ahead; the first key
-    // chunk must have landed before the first barrier publishes it
-    const bool key_wave = score_wave && role == 0;
-    if (key_wave) {
-        for (int s = 0; s < NSK - 1; ++s)
-            if (s < nk) issue_keys_any<C>(ts, stream + STREAMS * s, kring + s * C::K_BYTES, mring + s * C::M_STAGE);
-        wait_chunks_after<C::A_LOADS>(min(NSK - 2, nk - 1));
-    } else if (!score_wave) {
-        for (int s = 0; s < NSV - 1; ++s)
-            if (s < nk) issue_planes<C>(ts, stream + STREAMS * s, role - NSW, bring + s * C::B_STAGE);
+    if (score_wave) {
+        const float qs = a.softmax_scale * kLog2e;
+#pragma unroll
+        for (int rb = 0; rb < SRB; ++rb)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const float4 u0 = qraw[rb][b][0], u1 = qraw[rb][b][1];
+                const float x[8] = {u0.x * qs, u0.y * qs, u0.z * qs, u0.w * qs,
+                                    u1.x * qs, u1.y * qs, u1.z * qs, u1.w * qs};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qh[rb][b][e] = (_Float16)x[e];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ql[rb][b][e] = (_Float16)(x[e] - (float)qh[rb][b][e]);
+            }
     }
+    // the first key chunk must have landed before the barrier publishes it (the query
+    // loads, issued after the DMA, have been waited for above)
+    if (key_wave) wait_chunks_after<C::A_LOADS>(min(NSK - 2, nk - 1));
     __syncthreads();
 
     f4 O[NRB][VDB];  // value waves: rows 16 rb + 4j + i, dims HD * half + VDB * l16 + db
@@ -615,9 +628,10 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
     }
 
     // ---- merge the streams and finish the rows ----
+    constexpr int MQS = C::MQS, MRS = C::MRS;
     float* mw = reinterpret_cast<float*>(lds + C::OFF_STREAMS);  // [STREAMS][ROWS]
     float* lw = mw + STREAMS * ROWS;                              // [STREAMS][ROWS]
-    float* ob = lw + STREAMS * ROWS;                              // [2][ROWS][D]
+    float* ob = lw + STREAMS * ROWS;                              // [2][ROWS][MRS]
     if (score_wave) {
 #pragma unroll
         for (int rb = 0; rb < SRB; ++rb) {
@@ -630,9 +644,11 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
         }
     }
     __syncthreads();
-    // the value waves of stream s weight their rows by 2^(m_s - M)
+    // the value waves of stream s weight their rows by 2^(m_s - M); a lane's VDB
+    // consecutive dims lie inside one 32-dim quarter
     float fo[NRB][4];
-    const int dim0 = HD * (role - NSW) + VDB * l16;
+    const int dq = HD * (role - NSW) + VDB * l16;
+    const int qoff = (dq >> 5) * MQS + (dq & 31);
     if (!score_wave) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
@@ -643,40 +659,63 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
 #pragma unroll
                 for (int v = 0; v < STREAMS; ++v) M = fmaxf(M, mw[v * ROWS + row]);
                 const float mine = mw[stream * ROWS + row];
-                fo[rb][i] = mine == -INFINITY ? 0.0f : exp2f(mine - M);
+                fo[rb][i] = mine == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mine - M);
             }
         if (stream < 2) {
-            float* mybuf = ob + stream * ROWS * D;
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int db = 0; db < VDB; ++db)
-                        mybuf[(16 * rb + 4 * j + i) * D + dim0 + db] = O[rb][db][i] * fo[rb][i];
+                for (int i = 0; i < 4; ++i) {
+                    float* pp = ob + (stream * ROWS + 16 * rb + 4 * j + i) * MRS + qoff;
+                    if constexpr (VDB == 4)
+                        *reinterpret_cast<float4*>(pp) = make_float4(O[rb][0][i] * fo[rb][i], O[rb][1][i] * fo[rb][i],
+                                                                     O[rb][2][i] * fo[rb][i], O[rb][3][i] * fo[rb][i]);
+                    else
+                        *reinterpret_cast<float2*>(pp) = make_float2(O[rb][0][i] * fo[rb][i], O[rb][1][i] * fo[rb][i]);
+                }
         }
     }
     __syncthreads();
     if (!score_wave && stream >= 2) {
-        float* mybuf = ob + (stream - 2) * ROWS * D;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int db = 0; db < VDB; ++db)
-                    mybuf[(16 * rb + 4 * j + i) * D + dim0 + db] += O[rb][db][i] * fo[rb][i];
+            for (int i = 0; i < 4; ++i) {
+                float* pp = ob + ((stream - 2) * ROWS + 16 * rb + 4 * j + i) * MRS + qoff;
+                if constexpr (VDB == 4) {
+                    float4 u = *reinterpret_cast<const float4*>(pp);
+                    u.x += O[rb][0][i] * fo[rb][i];
+                    u.y += O[rb][1][i] * fo[rb][i];
+                    u.z += O[rb][2][i] * fo[rb][i];
+                    u.w += O[rb][3][i] * fo[rb][i];
+                    *reinterpret_cast<float4*>(pp) = u;
+                } else {
+                    float2 u = *reinterpret_cast<const float2*>(pp);
+                    u.x += O[rb][0][i] * fo[rb][i];
+                    u.y += O[rb][1][i] * fo[rb][i];
+                    *reinterpret_cast<float2*>(pp) = u;
+                }
+            }
     }
     __syncthreads();
 
-    // four threads per row, D/4 dimensions each; FWHT stages below D/4 in registers, the
-    // last two across the four threads
+    // four threads per row (a quad of lanes), D/4 consecutive dimensions each, inside one
+    // quarter; FWHT stages below D/4 in registers, the last two across the quad
     constexpr int QD = D / 4;
     const int row = tid >> 2, qtr = tid & 3;
     if (row < ROWS) {
         float x[QD];
+        const float* p0 = ob + row * MRS + ((qtr * QD) >> 5) * MQS + ((qtr * QD) & 31);
+        const float* p1 = p0 + ROWS * MRS;
 #pragma unroll
-        for (int e = 0; e < QD; ++e) x[e] = ob[row * D + qtr * QD + e] + ob[ROWS * D + row * D + qtr * QD + e];
+        for (int e = 0; e < QD; e += 4) {
+            const float4 u = *reinterpret_cast<const float4*>(p0 + e);
+            const float4 w = *reinterpret_cast<const float4*>(p1 + e);
+            x[e] = u.x + w.x;
+            x[e + 1] = u.y + w.y;
+            x[e + 2] = u.z + w.z;
+            x[e + 3] = u.w + w.w;
+        }
 #pragma unroll
         for (int hh = 1; hh < QD; hh <<= 1)
 #pragma unroll
@@ -686,13 +725,17 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
                     x[e] = u + v;
                     x[e + hh] = u - v;
                 }
+        // partner lane qtr ^ stp through a quad permutation (DPP): the lower lane of a
+        // pair keeps x + other, the upper one other - x
 #pragma unroll
         for (int stp = 1; stp <= 2; stp <<= 1) {
-            const bool upper = (qtr & stp) != 0;
+            const float sg = (qtr & stp) ? -1.0f : 1.0f;
 #pragma unroll
             for (int e = 0; e < QD; ++e) {
-                const float other = __shfl_xor(x[e], stp);
-                x[e] = upper ? other - x[e] : x[e] + other;
+                const int xi = __float_as_int(x[e]);
+                const int oi = stp == 1 ? __builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false)   // lanes 1,0,3,2
+                                        : __builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xF, 0xF, false);  // lanes 2,3,0,1
+                x[e] = __builtin_fmaf(sg, x[e], __int_as_float(oi));
             }
         }
         float M = -INFINITY;
@@ -702,7 +745,7 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
 #pragma unroll
         for (int v = 0; v < STREAMS; ++v) {
             const float mv = mw[v * ROWS + row];
-            if (mv != -INFINITY) L += lw[v * ROWS + row] * exp2f(mv - M);
+            if (mv != -INFINITY) L += lw[v * ROWS + row] * __builtin_amdgcn_exp2f(mv - M);
         }
         if (row < R) {
             const float inv = 1.0f / ((float)D * L * a.cb.fp16_scale);
