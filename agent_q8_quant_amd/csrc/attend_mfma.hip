@@ -270,7 +270,9 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
     constexpr int AL_STRIDE = C::AL_STRIDE;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    // from mbcnt (not from the thread index) so that the lane-derived values below can
+    // be recomputed where they are used instead of being held across the chunk loop
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int stream = w % STREAMS;
     const int role = w / STREAMS;                            // < NSW: score wave
@@ -396,6 +398,9 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
 
     if (score_wave) {
         // ===================== score waves =====================
+        // the score waves carry the longer dependency chain of a chunk step: their
+        // instructions go first when both kinds of wave are ready to issue
+        __builtin_amdgcn_s_setprio(1);
         // LDS offsets (within a stage) of the key fragments: token l16, dims 32b + 8j .. +7,
         // through the row swizzle
         // (token block tb adds 16 * D: the swizzle depends only on the low row bits)
@@ -701,8 +706,11 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
 
     // four threads per row (a quad of lanes), D/4 consecutive dimensions each, inside one
     // quarter; FWHT stages below D/4 in registers, the last two across the quad
+    // (the thread index is rebuilt from the lane id here rather than kept live, and
+    // spilled, across the chunk loop)
     constexpr int QD = D / 4;
-    const int row = tid >> 2, qtr = tid & 3;
+    const int ftid = 64 * w + lane;
+    const int row = ftid >> 2, qtr = ftid & 3;
     if (row < ROWS) {
         float x[QD];
         const float* p0 = ob + row * MRS + ((qtr * QD) >> 5) * MQS + ((qtr * QD) & 31);
