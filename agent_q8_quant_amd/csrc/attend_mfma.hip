@@ -28,8 +28,11 @@
 //   ring. One workgroup barrier per chunk step publishes keys and probabilities;
 // - a row's reference maximum is raised only when a score exceeds it by more than 8
 //   (log2 units); the score wave then passes per-row rescale factors to the value waves;
-// - at the end the streams' (m, l, acc) are merged through LDS and each row becomes
-//   H acc / (d l).
+// - start-up: the first chunks are requested, then the queries, and the queries are
+//   converted only after the lookup tables are built, so that the latencies overlap;
+//   score waves issue at a raised priority (their chain is the longer one);
+// - at the end the streams' (m, l, acc) are merged through LDS in a bank-padded layout and
+//   each row becomes H acc / (d l), the last two FWHT stages across a quad of lanes (DPP).
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
