@@ -10,7 +10,8 @@
 // Layout of the work (one workgroup per tile, four token streams, one per SIMD):
 // - the tile's tokens are cut into 32-token chunks (one value bit-plane group each);
 //   stream s takes chunks s, s+4, s+8, ...;
-// - each stream has score waves and two value waves, all on the stream's SIMD. A score
+// - each stream has score waves and two value waves (one in the small workgroups of at
+//   most 16 rows at d = 64), all on the stream's SIMD. A score
 //   wave owns a block of query rows: it computes S for its rows with
 //   v_mfma_f32_16x16x32_f16 (16 tokens x one 32-wide q8 block as A, codes converted to
 //   fp16 exactly; 16 query rows as B, the query split q = q_hi + q_lo in fp16 for ~22-bit
@@ -23,8 +24,8 @@
 //   one chunk behind the score waves. Four waves of similar register size per SIMD hide
 //   each other's latencies;
 // - the first score wave of a stream streams the keys, block scales and norms of its
-//   chunks into a four-deep LDS ring by direct-to-LDS DMA (256-byte aligned
-//   destinations); each value wave streams its half of the planes into a three-deep
+//   chunks into a four-deep (small workgroups: three-deep) LDS ring by direct-to-LDS DMA
+//   (256-byte aligned destinations); each value wave streams its share of the planes into a three-deep
 //   ring. One workgroup barrier per chunk step publishes keys and probabilities;
 // - a row's reference maximum is raised only when a score exceeds it by more than 8
 //   (log2 units); the score wave then passes per-row rescale factors to the value waves;
@@ -57,7 +58,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int STREAMS = 4;
 constexpr int CHUNK = 32;
-constexpr int NSK = 4;  // key ring depth (chunks)
 constexpr int NSV = 3;  // plane ring depth (chunks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -70,13 +70,19 @@ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 // the LDS small enough for two workgroups per CU).
 template <int D, int SRB, int NSW, bool LUT>
 struct MCfg {
+    // The small workgroups (the pair-table variant, at most 16 rows) run one value wave per
+    // stream and a three-deep key ring, so that three of them share a CU (LDS and
+    // registers): a pool of many small tiles then runs in one round.
+    static constexpr int NVW = LUT ? 2 : 1;            // value waves per stream
+    static constexpr int NSK = LUT ? 4 : 3;            // key ring depth (chunks)
+    static constexpr int WG_PER_CU = LUT ? 1 : 3;
     static constexpr int NB = D / 32;                  // q8 blocks per row
     static constexpr int NRB = SRB * NSW;              // 16-row blocks per tile
     static constexpr int ROWS = 16 * NRB;
-    static constexpr int WAVES = STREAMS * (NSW + 2);
+    static constexpr int WAVES = STREAMS * (NSW + NVW);
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int SLOTS = D / 16;               // 16-byte slots in a key row
-    static constexpr int HD = D / 2;                   // dimensions per value wave
+    static constexpr int HD = D / NVW;                 // dimensions per value wave
     static constexpr int VDB = HD / 16;                // 16-column blocks per value wave
     // Every DMA destination below is 256-byte aligned.
     // key stage: key codes, rows XOR-swizzled by 16-byte slot
@@ -87,12 +93,12 @@ struct MCfg {
     static constexpr int M_OFF_S = 0;
     static constexpr int M_OFF_N = 256;
     static constexpr int M_STAGE = 512;
-    // plane stage: [value wave][plane][HD] words, each value wave's half 256-B aligned
+    // plane stage: [value wave][plane][HD] words, each value wave's share 256-B aligned
     static constexpr int VH_BYTES = 3 * HD * 4;
     static constexpr int VH_SLOT = round_up(VH_BYTES, 256);
     static constexpr int V_LANES = VH_BYTES / 16;      // lanes of the one DMA instruction
     static constexpr int LPP = HD * 4 / 16;            // lanes per plane
-    static constexpr int B_STAGE = 2 * VH_SLOT;
+    static constexpr int B_STAGE = NVW * VH_SLOT;
     // probabilities p * n (fp16 A operand of P.V, one h8 per lane and row block) and the
     // per-row rescale factors, then one flag per score wave
     static constexpr int P_BYTES = NRB * 64 * 16;
@@ -125,7 +131,7 @@ struct MCfg {
     static_assert(S_LANES <= 64 && V_LANES <= 64, "one DMA instruction each");
     static_assert(MERGE_BYTES <= STREAMS * STREAM_BYTES, "merge area fits");
     static_assert(MQS % 4 == 0 && MRS % 4 == 0 && (2 * STREAMS * ROWS) % 4 == 0, "16-byte merge accesses");
-    static_assert(LDS <= 160 * 1024, "fits the LDS of one CU");
+    static_assert(WG_PER_CU * LDS <= 160 * 1024, "WG_PER_CU workgroups fit the LDS of one CU");
     static_assert(NSK <= 4 && NSV <= 4 && 3 * A_LOADS <= 63, "wait_chunks_after covers the rings");
     static_assert(S_BYTES <= 256 && N_BYTES <= 256 && K_BYTES % 256 == 0 && OFF_STREAMS % 256 == 0,
                   "256-byte aligned DMA destinations");
@@ -267,7 +273,9 @@ __device__ __forceinline__ void issue_planes(const TileSrc& ts, int c, int half,
 }
 
 template <int D, int SRB, int NSW, bool LUT>
-__global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(AttendArgs a) {
+__global__ __launch_bounds__((MCfg<D, SRB, NSW, LUT>::THREADS))
+__attribute__((amdgpu_waves_per_eu(MCfg<D, SRB, NSW, LUT>::WG_PER_CU * MCfg<D, SRB, NSW, LUT>::WAVES / STREAMS)))
+void k_attend_mfma(AttendArgs a) {
     using C = MCfg<D, SRB, NSW, LUT>;
     constexpr int NB = C::NB, NRB = C::NRB, ROWS = C::ROWS, VDB = C::VDB, HD = C::HD;
     constexpr int AL_STRIDE = C::AL_STRIDE;
@@ -309,10 +317,10 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
 
     // The start-up latencies overlap: the first DMA chunks, then the query loads, are in
     // flight while the lookup tables are built; the queries are converted afterwards.
-    // start streaming NSK - 1 key chunks and NSV - 1 plane chunks ahead
+    // start streaming C::NSK - 1 key chunks and NSV - 1 plane chunks ahead
     const bool key_wave = score_wave && role == 0;
     if (key_wave) {
-        for (int s = 0; s < NSK - 1; ++s)
+        for (int s = 0; s < C::NSK - 1; ++s)
             if (s < nk) issue_keys_any<C>(ts, stream + STREAMS * s, kring + s * C::K_BYTES, mring + s * C::M_STAGE);
     } else if (!score_wave) {
         for (int s = 0; s < NSV - 1; ++s)
@@ -390,7 +398,7 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
     }
     // the first key chunk must have landed before the barrier publishes it (the query
     // loads, issued after the DMA, have been waited for above)
-    if (key_wave) wait_chunks_after<C::A_LOADS>(min(NSK - 2, nk - 1));
+    if (key_wave) wait_chunks_after<C::A_LOADS>(min(C::NSK - 2, nk - 1));
     __syncthreads();
 
     f4 O[NRB][VDB];  // value waves: rows 16 rb + 4j + i, dims HD * half + VDB * l16 + db
@@ -419,15 +427,15 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
             if (k < nk) {
                 const int c = stream + STREAMS * k;
                 const int t0 = c * CHUNK;
-                if (key_wave && k + NSK - 1 < nk)
-                    issue_keys_any<C>(ts, c + STREAMS * (NSK - 1), kring + ((k + NSK - 1) % NSK) * C::K_BYTES,
-                                      mring + ((k + NSK - 1) % NSK) * C::M_STAGE);
+                if (key_wave && k + C::NSK - 1 < nk)
+                    issue_keys_any<C>(ts, c + STREAMS * (C::NSK - 1), kring + ((k + C::NSK - 1) % C::NSK) * C::K_BYTES,
+                                      mring + ((k + C::NSK - 1) % C::NSK) * C::M_STAGE);
                 // stage offset in LDS: wave-uniform, so every lane address below is one
                 // scalar + vector add
                 const uint32_t st_off = (uint32_t)__builtin_amdgcn_readfirstlane(
-                    (int)(C::OFF_STREAMS + stream * C::STREAM_BYTES + C::ST_OFF_K + (k % NSK) * C::K_BYTES));
+                    (int)(C::OFF_STREAMS + stream * C::STREAM_BYTES + C::ST_OFF_K + (k % C::NSK) * C::K_BYTES));
                 const uint32_t mt_off = (uint32_t)__builtin_amdgcn_readfirstlane(
-                    (int)(C::OFF_STREAMS + stream * C::STREAM_BYTES + C::ST_OFF_M + (k % NSK) * C::M_STAGE));
+                    (int)(C::OFF_STREAMS + stream * C::STREAM_BYTES + C::ST_OFF_M + (k % C::NSK) * C::M_STAGE));
                 const uint8_t* st = lds + st_off;
                 const uint8_t* mt = lds + mt_off;
                 const h4 n_lo = *reinterpret_cast<const h4*>(mt + C::M_OFF_N + 8 * j);
@@ -553,7 +561,7 @@ __global__ __launch_bounds__(64 * STREAMS * (NSW + 2), 1) void k_attend_mfma(Att
                     pb[(SRB * role + rb) * 64 + lane] = ph * nn;
                 }
                 // the next key chunk must have landed before the barrier publishes it
-                if (key_wave) wait_chunks_after<C::A_LOADS>(max(0, min(NSK - 2, nk - 2 - k)));
+                if (key_wave) wait_chunks_after<C::A_LOADS>(max(0, min(C::NSK - 2, nk - 2 - k)));
             }
             __syncthreads();
         }
