@@ -120,9 +120,12 @@ def test_append_writes_only_its_tokens():
 
 @pytest.mark.parametrize("path", PATHS, ids=["valu", "mfma"])
 @pytest.mark.parametrize("n_valid", [1, 31, 32, 33, 95, 257, 300])
-def test_prefix_decode(n_valid, path):
-    L, H, d, T = 2, 2, 128, 300
-    A, G = 15, 4
+@pytest.mark.parametrize("shape", [(2, 2, 128, 15, 4), (2, 3, 64, 5, 1)], ids=["d128_rows60", "d64_rows5"])
+def test_prefix_decode(n_valid, path, shape):
+    # d = 64 with at most 16 rows runs the small-workgroup instantiation (three-deep key
+    # ring, one value wave per stream)
+    L, H, d, A, G = shape
+    T = 300
     if path == pk.POLYKV_PATH_MFMA and A * G > 64:
         pytest.skip("rows")
     print("prefix", n_valid, path, flush=True)
