@@ -280,13 +280,15 @@ def test_determinism_stream_and_layer_range(path):
 
 
 @pytest.mark.parametrize("path", PATHS, ids=["valu", "mfma"])
-def test_long_context_single_tile(path):
+@pytest.mark.parametrize("shape", [(128, 5, 4), (64, 5, 1)], ids=["d128_rows20", "d64_rows5"])
+def test_long_context_single_tile(path, shape):
     """A 100,000-token tile (far past the pages' 7,194): offsets, chunk counts and the
     streams' merge at a length no workload reaches; the pool is compressed on the GPU and
-    compared with the oracle's compress (keys bit-exact) before the decode is checked."""
+    compared with the oracle's compress (keys bit-exact) before the decode is checked.
+    d = 64 with five rows runs the small-workgroup decode (three-deep key ring)."""
     _supported(path, CONFIGS[0])
-    L, H, d, T = 1, 1, 128, 100_000
-    A, G = 5, 4
+    d, A, G = shape
+    L, H, T = 1, 1, 100_000
     rng = np.random.default_rng(99)
     k = rng.standard_normal((L, H, T, d)).astype(np.float16)
     v = rng.standard_normal((L, H, T, d)).astype(np.float16)
