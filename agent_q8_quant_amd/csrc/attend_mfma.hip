@@ -10,22 +10,22 @@
 // Layout of the work (one workgroup per tile, four token streams, one per SIMD):
 // - the tile's tokens are cut into 32-token chunks (one value bit-plane group each);
 //   stream s takes chunks s, s+4, s+8, ...;
-// - each stream has score waves and two value waves (one in the small workgroups of at
-//   most 16 rows at d = 64), all on the stream's SIMD. A score
+// - each stream has score waves and two value waves, all on the stream's SIMD. A score
 //   wave owns a block of query rows: it computes S for its rows with
 //   v_mfma_f32_16x16x32_f16 (16 tokens x one 32-wide q8 block as A, codes converted to
 //   fp16 exactly; 16 query rows as B, the query split q = q_hi + q_lo in fp16 for ~22-bit
 //   precision), applies the block scales with v_fma_mix, runs a lazy-max online softmax
 //   in base 2 and writes p * n_t as fp16 to a double-buffered LDS slot. A value wave owns
 //   half of the head dimensions: it decodes the value bit-planes of its dimensions to
-//   fp16 centroids through a 4096-entry table (one nibble of each plane = 4 tokens; for
-//   small workgroups, through the 64-entry pair table it is built from, two tokens per
-//   lookup, so that two workgroups fit one CU) and accumulates P.V for every row in fp32,
-//   one chunk behind the score waves. Four waves of similar register size per SIMD hide
-//   each other's latencies;
+//   fp16 centroids through a 4096-entry table (one nibble of each plane = 4 tokens) and
+//   accumulates P.V for every row in fp32, one chunk behind the score waves. Four waves
+//   of similar register size per SIMD hide each other's latencies;
+// - small workgroups (d = 64, at most 16 rows) run one value wave per stream for all the
+//   dimensions, read the 64-entry pair table the big table is built from (two tokens per
+//   lookup) and use a three-deep key ring, so that three of them fit one CU;
 // - the first score wave of a stream streams the keys, block scales and norms of its
-//   chunks into a four-deep (small workgroups: three-deep) LDS ring by direct-to-LDS DMA
-//   (256-byte aligned destinations); each value wave streams its share of the planes into a three-deep
+//   chunks into a four-deep LDS ring by direct-to-LDS DMA (256-byte aligned
+//   destinations); each value wave streams its share of the planes into a three-deep
 //   ring. One workgroup barrier per chunk step publishes keys and probabilities;
 // - a row's reference maximum is raised only when a score exceeds it by more than 8
 //   (log2 units); the score wave then passes per-row rescale factors to the value waves;
