@@ -259,7 +259,8 @@ hipError_t launch_valu_t(const AttendArgs& a, hipStream_t s) {
     using Cfg = ValuCfg<D, NRQ>;
     const size_t lds = (size_t)Cfg::FLOATS * sizeof(float);
     auto kern = k_attend_valu<D, NRQ>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once((const void*)kern, (int)lds, lds_set);
     if (e != hipSuccess) return e;
     const uint32_t tiles = (uint32_t)a.layer_count * (uint32_t)a.g.n_kv_heads;
     hipLaunchKernelGGL(kern, dim3(tiles), dim3(256), lds, s, a);

@@ -55,13 +55,19 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int STREAMS = 4;
 constexpr int CHUNK = 32;
 constexpr int NSV = 3;  // plane ring depth (chunks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kSlack = 8.0f;  // log2 units a score may exceed the reference maximum
+// Reference maxima of the online softmax (log2 units): a row's reference puts the largest
+// p * n of the chunk that places it at 2^kPlace, and is raised when some p * n could exceed
+// 2^(kPlace + kSlack) or some p could exceed 2^kPmax.
+constexpr float kPlace = 6.0f;
+constexpr float kSlack = 8.0f;
+constexpr float kPmax = 64.0f;
 
 constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -75,6 +81,7 @@ struct MCfg {
     // registers): a pool of many small tiles then runs in one round.
     static constexpr int NVW = LUT ? 2 : 1;            // value waves per stream
     static constexpr int NSK = LUT ? 4 : 3;            // key ring depth (chunks)
+    static constexpr int K_PRE = 2;                    // key chunks requested before the first step
     static constexpr int WG_PER_CU = LUT ? 1 : 3;
     static constexpr int NB = D / 32;                  // q8 blocks per row
     static constexpr int NRB = SRB * NSW;              // 16-row blocks per tile
@@ -135,7 +142,7 @@ struct MCfg {
     static_assert(NSK <= 4 && NSV <= 4 && 3 * A_LOADS <= 63, "wait_chunks_after covers the rings");
     static_assert(S_BYTES <= 256 && N_BYTES <= 256 && K_BYTES % 256 == 0 && OFF_STREAMS % 256 == 0,
                   "256-byte aligned DMA destinations");
-    static_assert(4 * ROWS <= THREADS, "four finishing threads per row");
+    static_assert(16 * ROWS <= THREADS && D % 64 == 0, "sixteen finishing threads per row, whole float4 of dims each");
     static_assert(SLOTS <= 16 && 1024 % D == 0, "the key swizzle repeats every 1 KB");
 };
 
@@ -181,6 +188,12 @@ __device__ __forceinline__ float max_over_j(float x) {
     const uint32_t v = __float_as_uint(y);
     const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ uint32_t max_over_j_u32(uint32_t u) {
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t v = max(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(b[0], b[1]);
 }
 __device__ __forceinline__ float sum_over_j(float x) {
     const uint32_t u = __float_as_uint(x);
@@ -315,18 +328,7 @@ void k_attend_mfma(AttendArgs a) {
     float* albuf = reinterpret_cast<float*>(sbase + C::ST_OFF_AL);  // [2][AL_STRIDE]
     const size_t HG = (size_t)H * G;
 
-    // The start-up latencies overlap: the first DMA chunks, then the query loads, are in
-    // flight while the lookup tables are built; the queries are converted afterwards.
-    // start streaming C::NSK - 1 key chunks and NSV - 1 plane chunks ahead
     const bool key_wave = score_wave && role == 0;
-    if (key_wave) {
-        for (int s = 0; s < C::NSK - 1; ++s)
-            if (s < nk) issue_keys_any<C>(ts, stream + STREAMS * s, kring + s * C::K_BYTES, mring + s * C::M_STAGE);
-    } else if (!score_wave) {
-        for (int s = 0; s < NSV - 1; ++s)
-            if (s < nk) issue_planes<C>(ts, stream + STREAMS * s, role - NSW, bring + s * C::B_STAGE);
-    }
-
     // ---- score waves: queries (B operand). Lane holds row 16 rb + l16 of its row
     // blocks, dims 32b + 8j .. +7, times scale * log2(e), as fp16 hi + lo.
     h8 qh[SRB][NB], ql[SRB][NB];
@@ -351,6 +353,19 @@ void k_attend_mfma(AttendArgs a) {
                 for (int b = 0; b < NB; ++b) qraw[rb][b][0] = qraw[rb][b][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         }
+    }
+
+    // The start-up latencies overlap: the query loads go out first (nothing can be scored
+    // before they land), then the first chunks: K_PRE key chunks and NSV - 1 plane chunks
+    // (the key ring's remaining chunks follow in the first chunk step, which keeps the
+    // burst of requests at launch small); the lookup tables are built meanwhile, and the
+    // queries are converted afterwards.
+    if (key_wave) {
+        for (int s = 0; s < C::K_PRE; ++s)
+            if (s < nk) issue_keys_any<C>(ts, stream + STREAMS * s, kring + s * C::K_BYTES, mring + s * C::M_STAGE);
+    } else if (!score_wave) {
+        for (int s = 0; s < NSV - 1; ++s)
+            if (s < nk) issue_planes<C>(ts, stream + STREAMS * s, role - NSW, bring + s * C::B_STAGE);
     }
 
     // value lookup table, built in two steps. Pair table: entry x (6 bits: plane 0, 1 and 2
@@ -396,9 +411,8 @@ void k_attend_mfma(AttendArgs a) {
                 for (int e = 0; e < 8; ++e) ql[rb][b][e] = (_Float16)(x[e] - (float)qh[rb][b][e]);
             }
     }
-    // the first key chunk must have landed before the barrier publishes it (the query
-    // loads, issued after the DMA, have been waited for above)
-    if (key_wave) wait_chunks_after<C::A_LOADS>(min(C::NSK - 2, nk - 1));
+    // the first key chunk must have landed before the barrier publishes it
+    if (key_wave) wait_chunks_after<C::A_LOADS>(min(C::K_PRE - 1, nk - 1));
     __syncthreads();
 
     f4 O[NRB][VDB];  // value waves: rows 16 rb + 4j + i, dims HD * half + VDB * l16 + db
@@ -427,9 +441,15 @@ void k_attend_mfma(AttendArgs a) {
             if (k < nk) {
                 const int c = stream + STREAMS * k;
                 const int t0 = c * CHUNK;
-                if (key_wave && k + C::NSK - 1 < nk)
-                    issue_keys_any<C>(ts, c + STREAMS * (C::NSK - 1), kring + ((k + C::NSK - 1) % C::NSK) * C::K_BYTES,
-                                      mring + ((k + C::NSK - 1) % C::NSK) * C::M_STAGE);
+                if (key_wave) {
+                    // the rest of the ring's initial chunks, then one chunk per step, NSK - 1 ahead
+                    if (k == 0)
+                        for (int s2 = C::K_PRE; s2 < C::NSK - 1; ++s2)
+                            if (s2 < nk) issue_keys_any<C>(ts, stream + STREAMS * s2, kring + s2 * C::K_BYTES, mring + s2 * C::M_STAGE);
+                    if (k + C::NSK - 1 < nk)
+                        issue_keys_any<C>(ts, c + STREAMS * (C::NSK - 1), kring + ((k + C::NSK - 1) % C::NSK) * C::K_BYTES,
+                                          mring + ((k + C::NSK - 1) % C::NSK) * C::M_STAGE);
+                }
                 // stage offset in LDS: wave-uniform, so every lane address below is one
                 // scalar + vector add
                 const uint32_t st_off = (uint32_t)__builtin_amdgcn_readfirstlane(
@@ -454,7 +474,7 @@ void k_attend_mfma(AttendArgs a) {
                     for (int v = 0; v < (NB + 1) / 2; ++v) scv[v] = sp[v];
 #pragma unroll
                     for (int rb = 0; rb < SRB; ++rb) {
-                        const float init = first ? 0.0f : -(m_ref[rb] + kSlack);
+                        const float init = first ? 0.0f : -m_ref[rb];
                         S[tb][rb] = f4{init, init, init, init};
                     }
                     // two-stage pipeline over the q8 blocks: block b+1's conversion and its
@@ -493,9 +513,17 @@ void k_attend_mfma(AttendArgs a) {
                         }
                     }
                 }
-                // reference maxima: exact on the first chunk; afterwards raised only when a
-                // score exceeds m_ref + slack (then the value waves rescale these rows).
-                // Tokens past T carry the last token's score, so they never raise it.
+                // Probabilities p = 2^(score - m) with one reference m per row; the P.V operand
+                // is p * n rounded once to fp16 (n the token's value norm), the row sums take
+                // p in fp32. m is placed so that the row's largest p * n in the chunk that
+                // places it is 2^kPlace, and raised only when some p * n could exceed
+                // 2^(kPlace + kSlack) or some p could exceed 2^kPmax: the operand then holds
+                // every weight within 2^-(14 + kPlace) of the row's largest as a normal fp16
+                // number and never overflows, and p stays finite (zero norms included). The
+                // per-chunk check is conservative: the largest score - m of the wave's rows
+                // against kPlace + kSlack - log2 of the chunk's largest norm. The tile's last
+                // chunk always takes the exact path (its norm slots past T may hold any bits;
+                // its rows past T repeat the last token, so they never raise m).
                 float mx = -INFINITY;
 #pragma unroll
                 for (int rb = 0; rb < SRB; ++rb)
@@ -503,25 +531,40 @@ void k_attend_mfma(AttendArgs a) {
                     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[tb][rb][i]);
+                // the chunk's largest norm: non-negative fp16 bit patterns order as integers
+                const u16x4 nmv = __builtin_elementwise_max(__builtin_bit_cast(u16x4, n_lo), __builtin_bit_cast(u16x4, n_hi));
+                const uint32_t nmb = max_over_j_u32(max(max((uint32_t)nmv[0], (uint32_t)nmv[1]),
+                                                        max((uint32_t)nmv[2], (uint32_t)nmv[3])));
+                const float thr = fminf(kPlace + kSlack - __builtin_log2f((float)__builtin_bit_cast(_Float16, (uint16_t)nmb)), kPmax);
                 float* al = albuf + (k & 1) * AL_STRIDE;
-                const bool raise = __any(first || mx > 0.0f);
+                const bool raise = __any(first || t0 + CHUNK > T || mx > thr);
                 if (raise) {
                     asm volatile("" ::: "memory");  // rare: keep it out of the common path
+                    // norms and weights of the lane's tokens (slots past T may hold any bits)
+                    const h8 nr = {n_lo[0], n_lo[1], n_lo[2], n_lo[3], n_hi[0], n_hi[1], n_hi[2], n_hi[3]};
+                    const h8 wt = {m_lo[0], m_lo[1], m_lo[2], m_lo[3], m_hi[0], m_hi[1], m_hi[2], m_hi[3]};
 #pragma unroll
                     for (int rb = 0; rb < SRB; ++rb) {
-                        float cm = -INFINITY;
+                        // the row's largest log2(p * n) and largest score - m in this chunk
+                        float cw = -INFINITY, cs = -INFINITY;
 #pragma unroll
                         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) cm = fmaxf(cm, S[tb][rb][i]);
-                        cm = max_over_j(cm);
+                            for (int i = 0; i < 4; ++i) {
+                                cs = fmaxf(cs, S[tb][rb][i]);
+                                cw = fmaxf(cw, wt[4 * tb + i] != (_Float16)0.0f ? S[tb][rb][i] + __builtin_log2f((float)nr[4 * tb + i]) : -INFINITY);
+                            }
+                        cw = max_over_j(cw);
+                        cs = max_over_j(cs);
+                        // zero norms give -inf in cw; the second term keeps p <= 2^kPmax
+                        const float want = fmaxf(cw - kPlace, cs - kPmax);
                         float shift, alpha;
                         if (first) {
-                            m_ref[rb] = cm;
-                            shift = cm + kSlack;
+                            shift = want;
+                            m_ref[rb] = shift;
                             alpha = 1.0f;
                         } else {
-                            shift = fmaxf(cm, 0.0f);
+                            shift = (cw > kPlace + kSlack || cs > kPmax) ? want : 0.0f;
                             m_ref[rb] += shift;
                             alpha = __builtin_amdgcn_exp2f(-shift);
                             l_run[rb] *= alpha;
@@ -534,8 +577,7 @@ void k_attend_mfma(AttendArgs a) {
                     }
                 }
                 if (lane == 0) al[ROWS + role] = (raise && !first) ? 1.0f : 0.0f;
-                // probabilities (scaled by 2^-slack) in fp16; row sums of the weighted fp16
-                // probabilities; P.V operand p * n * weight
+                // p into the row sums (weight 0 past T), p * n into the P.V operand
                 const h8 wt = {m_lo[0], m_lo[1], m_lo[2], m_lo[3], m_hi[0], m_hi[1], m_hi[2], m_hi[3]};
                 h8 nv = h8{n_lo[0], n_lo[1], n_lo[2], n_lo[3], n_hi[0], n_hi[1], n_hi[2], n_hi[3]};
                 if (t0 + CHUNK > T) {
@@ -544,21 +586,21 @@ void k_attend_mfma(AttendArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) nv[e] = wt[e] != (_Float16)0.0f ? nv[e] : (_Float16)0.0f;
                 }
-                const h8 nn = nv * wt;
                 h8* pb = pbuf + (k & 1) * NRB * 64;
 #pragma unroll
                 for (int rb = 0; rb < SRB; ++rb) {
                     h8 ph;
+                    float l = l_run[rb];
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) ph[4 * tb + i] = (_Float16)__builtin_amdgcn_exp2f(S[tb][rb][i]);
-                    float l = l_run[rb];
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2)
-                        l = __builtin_amdgcn_fdot2(h2{ph[e], ph[e + 1]}, h2{wt[e], wt[e + 1]}, l, false);
+                        for (int i = 0; i < 4; ++i) {
+                            const float p = __builtin_amdgcn_exp2f(S[tb][rb][i]);
+                            l = __builtin_fmaf(p, (float)wt[4 * tb + i], l);
+                            ph[4 * tb + i] = (_Float16)(p * (float)nv[4 * tb + i]);
+                        }
                     l_run[rb] = l;
-                    pb[(SRB * role + rb) * 64 + lane] = ph * nn;
+                    pb[(SRB * role + rb) * 64 + lane] = ph;
                 }
                 // the next key chunk must have landed before the barrier publishes it
                 if (key_wave) wait_chunks_after<C::A_LOADS>(max(0, min(C::NSK - 2, nk - 2 - k)));
@@ -715,67 +757,82 @@ void k_attend_mfma(AttendArgs a) {
     }
     __syncthreads();
 
-    // four threads per row (a quad of lanes), D/4 consecutive dimensions each, inside one
-    // quarter; FWHT stages below D/4 in registers, the last two across the quad
-    // (the thread index is rebuilt from the lane id here rather than kept live, and
-    // spilled, across the chunk loop)
-    constexpr int QD = D / 4;
-    const int ftid = 64 * w + lane;
-    const int row = ftid >> 2, qtr = ftid & 3;
-    if (row < ROWS) {
-        float x[QD];
-        const float* p0 = ob + row * MRS + ((qtr * QD) >> 5) * MQS + ((qtr * QD) & 31);
+    // Sixteen threads per row, every wave of the workgroup: lane q + 4 a + 16 b of wave w
+    // (q, a, b in 0..3) holds dims FD * (q + 4 b) .. + FD - 1 of row 4 w + a. The FWHT stages
+    // below FD run in registers; the four above, partners lane ^ 1 and ^ 2 (a quad
+    // permutation, DPP) and lane ^ 16 and ^ 32 (row swaps), across lanes. (The indices are
+    // rebuilt from the lane id here rather than kept live, and spilled, across the loop.)
+    constexpr int FD = D / 16;
+    const int fq = lane & 3, fa = (lane >> 2) & 3, fb = lane >> 4;
+    const int ft = fq + 4 * fb;
+    const int row = 4 * w + fa;
+    if (4 * w < ROWS) {
+        float x[FD];
+        const int d0 = FD * ft;
+        const float* p0 = ob + min(row, ROWS - 1) * MRS + (d0 >> 5) * MQS + (d0 & 31);
         const float* p1 = p0 + ROWS * MRS;
 #pragma unroll
-        for (int e = 0; e < QD; e += 4) {
+        for (int e = 0; e < FD; e += 4) {
             const float4 u = *reinterpret_cast<const float4*>(p0 + e);
-            const float4 w = *reinterpret_cast<const float4*>(p1 + e);
-            x[e] = u.x + w.x;
-            x[e + 1] = u.y + w.y;
-            x[e + 2] = u.z + w.z;
-            x[e + 3] = u.w + w.w;
+            const float4 v = *reinterpret_cast<const float4*>(p1 + e);
+            x[e] = u.x + v.x;
+            x[e + 1] = u.y + v.y;
+            x[e + 2] = u.z + v.z;
+            x[e + 3] = u.w + v.w;
         }
 #pragma unroll
-        for (int hh = 1; hh < QD; hh <<= 1)
+        for (int hh = 1; hh < FD; hh <<= 1)
 #pragma unroll
-            for (int e = 0; e < QD; ++e)
+            for (int e = 0; e < FD; ++e)
                 if (!(e & hh)) {
                     const float u = x[e], v = x[e + hh];
                     x[e] = u + v;
                     x[e + hh] = u - v;
                 }
-        // partner lane qtr ^ stp through a quad permutation (DPP): the lower lane of a
-        // pair keeps x + other, the upper one other - x
+        // the lower lane of a pair keeps own + other, the upper one other - own
 #pragma unroll
         for (int stp = 1; stp <= 2; stp <<= 1) {
-            const float sg = (qtr & stp) ? -1.0f : 1.0f;
+            const float sg = (fq & stp) ? -1.0f : 1.0f;
 #pragma unroll
-            for (int e = 0; e < QD; ++e) {
+            for (int e = 0; e < FD; ++e) {
                 const int xi = __float_as_int(x[e]);
                 const int oi = stp == 1 ? __builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false)   // lanes 1,0,3,2
                                         : __builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xF, 0xF, false);  // lanes 2,3,0,1
                 x[e] = __builtin_fmaf(sg, x[e], __int_as_float(oi));
             }
         }
-        float M = -INFINITY;
+        // row swaps: the first result is the lower lane's value, the second the upper's
 #pragma unroll
-        for (int v = 0; v < STREAMS; ++v) M = fmaxf(M, mw[v * ROWS + row]);
-        float L = 0.0f;
+        for (int e = 0; e < FD; ++e) {
+            const uint32_t xu = __float_as_uint(x[e]);
+            const auto r = __builtin_amdgcn_permlane16_swap(xu, xu, false, false);
+            x[e] = __builtin_fmaf((fb & 1) ? -1.0f : 1.0f, __uint_as_float(r[1]), __uint_as_float(r[0]));
+        }
 #pragma unroll
-        for (int v = 0; v < STREAMS; ++v) {
-            const float mv = mw[v * ROWS + row];
-            if (mv != -INFINITY) L += lw[v * ROWS + row] * __builtin_amdgcn_exp2f(mv - M);
+        for (int e = 0; e < FD; ++e) {
+            const uint32_t xu = __float_as_uint(x[e]);
+            const auto r = __builtin_amdgcn_permlane32_swap(xu, xu, false, false);
+            x[e] = __builtin_fmaf((fb & 2) ? -1.0f : 1.0f, __uint_as_float(r[1]), __uint_as_float(r[0]));
         }
         if (row < R) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < STREAMS; ++v) M = fmaxf(M, mw[v * ROWS + row]);
+            float L = 0.0f;
+#pragma unroll
+            for (int v = 0; v < STREAMS; ++v) {
+                const float mv = mw[v * ROWS + row];
+                if (mv != -INFINITY) L += lw[v * ROWS + row] * __builtin_amdgcn_exp2f(mv - M);
+            }
             const float inv = 1.0f / ((float)D * L * a.cb.fp16_scale);
             const int ag = row / G, jj = row - ag * G;
-            // scores are in log2 units and every p carries 2^-(m + slack)
-            if (a.lse && qtr == 0)
+            // scores are in log2 units and every p carries 2^-m
+            if (a.lse && ft == 0)
                 a.lse[((size_t)l_local * A + ag) * HG + (size_t)h * G + jj] =
-                    kLn2 * (M + kSlack + __builtin_log2f(L));
-            float* o = a.out + (((size_t)l_local * A + ag) * HG + (size_t)h * G + jj) * D + qtr * QD;
+                    kLn2 * (M + __builtin_log2f(L));
+            float* o = a.out + (((size_t)l_local * A + ag) * HG + (size_t)h * G + jj) * D + d0;
 #pragma unroll
-            for (int e = 0; e < QD; e += 4)
+            for (int e = 0; e < FD; e += 4)
                 *reinterpret_cast<float4*>(o + e) = make_float4(x[e] * inv, x[e + 1] * inv, x[e + 2] * inv, x[e + 3] * inv);
         }
     }
@@ -785,7 +842,8 @@ template <int D, int SRB, int NSW, bool LUT = true>
 hipError_t launch_t(const AttendArgs& a, hipStream_t s) {
     using C = MCfg<D, SRB, NSW, LUT>;
     auto kern = k_attend_mfma<D, SRB, NSW, LUT>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once((const void*)kern, C::LDS, lds_set);
     if (e != hipSuccess) return e;
     const uint32_t tiles = (uint32_t)a.layer_count * (uint32_t)a.g.n_kv_heads;
     hipLaunchKernelGGL(kern, dim3(tiles), dim3(C::THREADS), C::LDS, s, a);

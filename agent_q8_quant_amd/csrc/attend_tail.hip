@@ -196,7 +196,8 @@ template <int D>
 hipError_t launch_tail_t(const TailArgs& a, hipStream_t s) {
     using C = TailCfg<D>;
     auto kern = k_attend_tail<D>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once((const void*)kern, C::LDS, lds_set);
     if (e != hipSuccess) return e;
     const uint32_t blocks = (uint32_t)a.layer_count * (uint32_t)a.n_agents * (uint32_t)a.n_kv_heads;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), C::LDS, s, a);

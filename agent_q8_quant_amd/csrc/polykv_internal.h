@@ -5,6 +5,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "polykv.h"
 
 namespace polykv {
@@ -17,6 +19,20 @@ struct PoolGeom {
     uint64_t v_planes_off, v_planes_stride;
     uint64_t v_norms_off, v_norms_stride;
 };
+
+// Raise a kernel's dynamic LDS limit once per device. The attribute stays set for the
+// kernel on that device, so later launches skip the call. `done` is the caller's flag word
+// for that kernel (bit d: device d done); devices past 63 set it on every launch.
+inline hipError_t lds_limit_once(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 inline PoolGeom make_geom(const polykv_layout_t& l) {
     PoolGeom g;

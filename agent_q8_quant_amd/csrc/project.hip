@@ -249,7 +249,8 @@ template <int D, int MODE>
 hipError_t launch_t(const PjArgs& a, int nz, hipStream_t s) {
     using C = PjCfg<D>;
     auto kern = k_project<D, MODE>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once((const void*)kern, C::LDS, lds_set);
     if (e != hipSuccess) return e;
     dim3 grid((a.n_tok + BM - 1) / BM, a.n_heads, nz);
     hipLaunchKernelGGL(kern, grid, dim3(C::THREADS), C::LDS, s, a);

@@ -95,12 +95,16 @@ typedef struct {
 } polykv_codebook_t;
 
 /*
- * Fill *out with the pool layout for *shape. Host only; touches no device.
- * Errors: NULL, SHAPE.
+ * Fill *out with the pool layout for *shape. PolyKV, Abstract: the compressed K/V cache
+ * is written a single time into one shared pool that every agent then reads; this fixes
+ * where each part of that pool lives (the four regions above). Host only; touches no
+ * device. Errors: NULL, SHAPE.
  */
 int polykv_pool_layout(const polykv_shape_t* shape, polykv_layout_t* out);
 
 /*
+ * PolyKV, Abstract: values are quantised with 3-bit Lloyd-Max codes whose centroids are
+ * fitted to the standard normal distribution (after the Hadamard rotation).
  * Fill *out with the library's Lloyd-Max codebook for N(0,1): Lloyd's iteration run in
  * fp64 to a fixed point (centroids = conditional means of their cells, boundaries =
  * midpoints), made exactly symmetric, centroids rounded to float32, boundaries = fp64
@@ -110,7 +114,8 @@ int polykv_pool_layout(const polykv_shape_t* shape, polykv_layout_t* out);
 int polykv_codebook_default(polykv_codebook_t* out);
 
 /*
- * q8_0-compress keys into the pool (the "Keys are quantized at int8 (q8_0)" step).
+ * q8_0-compress keys into the pool. PolyKV, Abstract: keys are stored as 8-bit integers
+ * in the q8_0 format, which keeps the softmax over the shared pool stable.
  *  k_fp16: device, IEEE binary16, contiguous [layer_count][n_kv_heads][n_tokens][head_dim]
  *          holding pool layers [layer_begin, layer_begin + layer_count); 16-B aligned.
  *  pool:   device, layout->total_bytes, 256-B aligned; only the k_codes and k_scales
@@ -228,9 +233,9 @@ size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_ag
                                      int32_t gqa, int32_t layer_count);
 
 /*
- * One decode step of every agent against the shared pool (the "N independent agent
- * contexts" reading one compressed pool). The pool is only read, so any number of calls
- * may run concurrently on one pool.
+ * One decode step of every agent against the shared pool. PolyKV, Abstract: one compressed
+ * pool serves several separate agent contexts at once. The pool is only read, so any
+ * number of calls may run concurrently on one pool.
  *  q:   device fp32 [layer_count][n_agents][n_kv_heads * gqa][head_dim], 16-B aligned;
  *       query head j of an agent attends KV head j / gqa.
  *  out: device fp32, same shape as q; every element is written.

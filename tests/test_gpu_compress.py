@@ -206,3 +206,34 @@ def test_non_default_stream_and_determinism():
         pools.append(pool)
     s.synchronize()
     assert torch.equal(pools[0], pools[1])
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS[1], CONFIGS[3]], ids=lambda c: c.name)
+def test_concurrent_key_and_value_compress(cfg):
+    """polykv_compress_k and polykv_compress_v write disjoint regions of the pool, so they may
+    run at the same time: launched on two streams with no order between them (each of several
+    rounds into a fresh copy of a garbage-filled pool), the pool is byte-identical to the
+    one written by the two calls in sequence."""
+    _say("concurrent compress", cfg.name)
+    lay = layout_for(cfg)
+    k, v = upload_kv(cfg)
+    base = new_pool(lay, fill=0x77)
+    seq = base.clone()
+    pk.polykv_compress_k(k, seq, lay)
+    pk.polykv_compress_v(v, seq, lay)
+    torch.cuda.synchronize()
+    sk, sv = torch.cuda.Stream(), torch.cuda.Stream()
+    for r in range(3):
+        pool = base.clone()
+        torch.cuda.synchronize()
+        # the value compress first on its stream in odd rounds, so both orders of issue occur
+        order = [(sv, lambda: pk.polykv_compress_v(v, pool, lay, stream=sv)),
+                 (sk, lambda: pk.polykv_compress_k(k, pool, lay, stream=sk))]
+        if r % 2 == 0:
+            order.reverse()
+        for st, fn in order:
+            with torch.cuda.stream(st):
+                fn()
+        sk.synchronize()
+        sv.synchronize()
+        assert torch.equal(pool, seq), "round %d" % r

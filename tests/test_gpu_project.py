@@ -129,3 +129,91 @@ def test_full_size_llama_layer():
     vg = v.cpu().numpy()[:, rows]
     check_projection(kg, x[rows], wk, H, d)
     check_projection(vg, x[rows], wv, H, d)
+
+
+# ---- the fused pool against the oracle ------------------------------------------------
+
+def _exact_inputs(n_tok, hidden, H, d, seed):
+    """Operands whose fp32 accumulation is exact in any order: x holds integers in [-8, 8]
+    and the weights integers in [-64, 64] times 2^-10, so every product and every partial
+    sum is a multiple of 2^-10 below 2^11 in magnitude (hidden <= 4096): at most 21
+    significant bits. The GPU's fp32 sum is then the exact sum, and its one rounding to
+    fp16 is the oracle's RNE16 of the fp64 product."""
+    assert hidden <= 4096
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-8, 9, (n_tok, hidden)).astype(np.float16)
+    wk = (rng.integers(-64, 65, (H * d, hidden)) * 2.0 ** -10).astype(np.float16)
+    wv = (rng.integers(-64, 65, (H * d, hidden)) * 2.0 ** -10).astype(np.float16)
+    return x, wk, wv
+
+
+def _check_chunk_against_oracle(pool, lay, layer, tb, x, wk, wv):
+    """The chunk's tokens of one layer in the GPU pool against the oracle's compression of
+    the oracle's fp16 projection: key codes and scales bit-exact, value codes per the
+    boundary rule, norms within one fp16 ulp."""
+    from gpu_helpers import B32, V_BOUNDARY_WINDOW, V_MISMATCH_FRACTION, check_norms, read_pool
+    s = lay.shape
+    H, d = s.n_kv_heads, s.head_dim
+    n = x.shape[0]
+    k16 = oracle.project_fp16(x, wk, H, d)[None]      # [1][H][n][d]
+    v16 = oracle.project_fp16(x, wv, H, d)[None]
+    want = oracle.compress_pool(k16, v16, B32)
+    got = read_pool(pool, lay)
+    tiles = slice(layer * H, (layer + 1) * H)
+    toks = slice(tb, tb + n)
+    assert np.array_equal(got["k_codes"][tiles][:, toks], want["k_codes"][0])
+    assert np.array_equal(got["k_scales"][tiles][:, toks].view(np.uint16), want["k_scales"][0].view(np.uint16))
+    codes = oracle.unpack_v_planes(got["v_planes"][tiles], s.n_tokens)[:, toks]   # [H][n][d]
+    diff = np.argwhere(codes != want["v_codes"][0])
+    b = B32.astype(np.float64)
+    for h, t, i in diff:
+        y = oracle.rotated_coordinates(v16[0, h, t])[i]
+        assert np.min(np.abs(y - b)) < V_BOUNDARY_WINDOW, (h, t, i, y)
+    assert len(diff) <= V_MISMATCH_FRACTION * codes.size, len(diff)
+    check_norms(got["v_norms"][tiles][:, toks], want["v_norms"][0])
+    return len(diff)
+
+
+@pytest.mark.parametrize("case", [(2, 3, 64, 300, 256, 0, 300, 1), (2, 2, 128, 600, 128, 64, 100, 0),
+                                  (1, 1, 128, 256, 64, 128, 128, 0), (1, 2, 64, 97, 512, 32, 65, 0)],
+                         ids=lambda c: "L%dH%dd%dT%dK%d_at%d_n%d_l%d" % c)
+def test_fused_pool_equals_oracle(case):
+    """polykv_project_compress against oracle.compress_pool(oracle.project_fp16(x, w)) on
+    operands whose fp16 projection is exact, in a garbage-filled pool."""
+    L, H, d, T, hidden, tb, n, layer = case
+    print("fused vs oracle", case, flush=True)
+    x, wk, wv = _exact_inputs(n, hidden, H, d, seed=T + n + 1)
+    lay = pk.polykv_pool_layout(L, H, d, T)
+    img = np.random.default_rng(11).integers(0, 256, lay.total_bytes, dtype=np.uint8)
+    pool = torch.from_numpy(img).to(device())
+    pk.polykv_project_compress(_dev(x), _dev(wk), _dev(wv), pool, lay, layer, tb)
+    torch.cuda.synchronize()
+    _check_chunk_against_oracle(pool, lay, layer, tb, x, wk, wv)
+
+
+def test_fused_llama_layer_against_oracle_and_decode():
+    """One Llama-3-8B layer at 4,096 tokens (hidden 4096, 8 KV heads of 128) through the fused
+    kernel: the pool against the oracle's projection + compression, then the 15-agent GQA-4
+    decode of that pool against the oracle's attention over the same pool."""
+    from gpu_helpers import C32, DECODE_REL_TOL, read_pool, row_rel_err
+    n, hidden, H, d, A, G = 4096, 4096, 8, 128, 15, 4
+    print("fused full size vs oracle", flush=True)
+    x, wk, wv = _exact_inputs(n, hidden, H, d, seed=5)
+    lay = pk.polykv_pool_layout(1, H, d, n)
+    pool = new_pool(lay, fill=0x3C)
+    pk.polykv_project_compress(_dev(x), _dev(wk), _dev(wv), pool, lay, 0, 0)
+    torch.cuda.synchronize()
+    nd = _check_chunk_against_oracle(pool, lay, 0, 0, x, wk, wv)
+    print("  value codes differing from the oracle: %d" % nd, flush=True)
+    got = read_pool(pool, lay)
+    gp = {"k_codes": got["k_codes"].reshape(1, H, n, d), "k_scales": got["k_scales"].reshape(1, H, n, d // 32),
+          "v_planes": got["v_planes"].reshape(1, H, -1, 3, d), "v_norms": got["v_norms"].reshape(1, H, n)}
+    kh, vh = oracle.dequant_pool(gp, C32, n)
+    qn = np.random.default_rng(6).standard_normal((1, A, H * G, d)).astype(np.float32)
+    q = _dev(qn)
+    out = torch.full_like(q, float("nan"))
+    pk.polykv_attend_shared(pool, lay, q, out, A, G, d ** -0.5)
+    ref = oracle.shared_pool_decode(qn, kh, vh, G, d ** -0.5)
+    err = row_rel_err(out.cpu().numpy(), ref)
+    print("  decode worst row error %.3e" % err, flush=True)
+    assert err <= DECODE_REL_TOL
