@@ -137,12 +137,13 @@ struct MCfg {
     static_assert(K_BYTES % 1024 == 0, "key stage is whole DMA instructions");
     static_assert(S_LANES <= 64 && V_LANES <= 64, "one DMA instruction each");
     static_assert(MERGE_BYTES <= STREAMS * STREAM_BYTES, "merge area fits");
+    static_assert(!(LUT && NRB == STREAMS) || 2 * NRB * NB * 64 * 16 <= LUT_BYTES, "shared query halves fit the table area");
     static_assert(MQS % 4 == 0 && MRS % 4 == 0 && (2 * STREAMS * ROWS) % 4 == 0, "16-byte merge accesses");
     static_assert(WG_PER_CU * LDS <= 160 * 1024, "WG_PER_CU workgroups fit the LDS of one CU");
     static_assert(NSK <= 4 && NSV <= 4 && 3 * A_LOADS <= 63, "wait_chunks_after covers the rings");
     static_assert(S_BYTES <= 256 && N_BYTES <= 256 && K_BYTES % 256 == 0 && OFF_STREAMS % 256 == 0,
                   "256-byte aligned DMA destinations");
-    static_assert(16 * ROWS <= THREADS && D % 64 == 0, "sixteen finishing threads per row, whole float4 of dims each");
+    static_assert(ROWS % 4 == 0 && D % 64 == 0, "whole rows per wave and whole float4 of dims per finishing thread");
     static_assert(SLOTS <= 16 && 1024 % D == 0, "the key swizzle repeats every 1 KB");
 };
 
@@ -330,27 +331,39 @@ void k_attend_mfma(AttendArgs a) {
 
     const bool key_wave = score_wave && role == 0;
     // ---- score waves: queries (B operand). Lane holds row 16 rb + l16 of its row
-    // blocks, dims 32b + 8j .. +7, times scale * log2(e), as fp16 hi + lo.
+    // blocks, dims 32b + 8j .. +7, times scale * log2(e), as fp16 hi + lo. With the big
+    // table (LUT) the query loads are shared: the first score wave of stream s loads row
+    // block s, splits it and writes both halves into the table's area, from which every
+    // score wave reads its own row blocks before the table is built (a tile's queries are
+    // loaded once instead of once per stream).
+    constexpr bool QSHARE = LUT && NRB == STREAMS;
+    constexpr int QRB = QSHARE ? 1 : SRB;     // row blocks loaded by this wave
     h8 qh[SRB][NB], ql[SRB][NB];
     float m_ref[SRB], l_run[SRB];
-    float4 qraw[SRB][NB][2];
+    float4 qraw[QRB][NB][2];
+    const bool q_loader = score_wave && (!QSHARE || role == 0);
     if (score_wave) {
 #pragma unroll
         for (int rb = 0; rb < SRB; ++rb) {
             m_ref[rb] = -INFINITY;
             l_run[rb] = 0.0f;
-            const int r = 16 * (SRB * role + rb) + l16;
+        }
+    }
+    if (q_loader) {
+#pragma unroll
+        for (int qb = 0; qb < QRB; ++qb) {
+            const int r = 16 * (QSHARE ? stream : SRB * role + qb) + l16;
             if (r < R) {
                 const int ag = r / G, jj = r - ag * G;
                 const float* qrow = a.q + (((size_t)l_local * A + ag) * HG + (size_t)h * G + jj) * D;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    qraw[rb][b][0] = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * j);
-                    qraw[rb][b][1] = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * j + 4);
+                    qraw[qb][b][0] = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * j);
+                    qraw[qb][b][1] = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * j + 4);
                 }
             } else {
 #pragma unroll
-                for (int b = 0; b < NB; ++b) qraw[rb][b][0] = qraw[rb][b][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                for (int b = 0; b < NB; ++b) qraw[qb][b][0] = qraw[qb][b][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         }
     }
@@ -386,7 +399,44 @@ void k_attend_mfma(AttendArgs a) {
         reinterpret_cast<_Float16*>(lds + C::OFF_MASK)[tid] =
             (!tail || (NC - 1) * CHUNK + t < T) ? (_Float16)1.0f : (_Float16)0.0f;
     }
-    __syncthreads();  // pair table complete
+    // split the loaded queries into fp16 hi + lo
+    h8* qsh = reinterpret_cast<h8*>(lds + C::OFF_LUT);  // shared halves: [hi, lo][rb][b][lane]
+    if (q_loader) {
+        const float qs = a.softmax_scale * kLog2e;
+#pragma unroll
+        for (int qb = 0; qb < QRB; ++qb)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const float4 u0 = qraw[qb][b][0], u1 = qraw[qb][b][1];
+                const float x[8] = {u0.x * qs, u0.y * qs, u0.z * qs, u0.w * qs,
+                                    u1.x * qs, u1.y * qs, u1.z * qs, u1.w * qs};
+                h8 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hi[e] = (_Float16)x[e];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) lo[e] = (_Float16)(x[e] - (float)hi[e]);
+                if constexpr (QSHARE) {
+                    qsh[(stream * NB + b) * 64 + lane] = hi;
+                    qsh[((NRB + stream) * NB + b) * 64 + lane] = lo;
+                } else {
+                    qh[qb][b] = hi;
+                    ql[qb][b] = lo;
+                }
+            }
+    }
+    __syncthreads();  // pair table (and shared query halves) complete
+    if constexpr (QSHARE) {
+        if (score_wave) {
+#pragma unroll
+            for (int rb = 0; rb < SRB; ++rb)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    qh[rb][b] = qsh[((SRB * role + rb) * NB + b) * 64 + lane];
+                    ql[rb][b] = qsh[((NRB + SRB * role + rb) * NB + b) * 64 + lane];
+                }
+        }
+        __syncthreads();  // query halves read before the table overwrites them
+    }
     if constexpr (LUT) {
         const uint32_t* pair = reinterpret_cast<const uint32_t*>(lds + C::OFF_PAIR);
         uint2* lut = reinterpret_cast<uint2*>(lds + C::OFF_LUT);
@@ -395,21 +445,6 @@ void k_attend_mfma(AttendArgs a) {
             const uint32_t i23 = ((e >> 2) & 3) | ((e >> 4) & 0xC) | ((e >> 6) & 0x30);
             lut[e] = make_uint2(pair[i01], pair[i23]);
         }
-    }
-    if (score_wave) {
-        const float qs = a.softmax_scale * kLog2e;
-#pragma unroll
-        for (int rb = 0; rb < SRB; ++rb)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float4 u0 = qraw[rb][b][0], u1 = qraw[rb][b][1];
-                const float x[8] = {u0.x * qs, u0.y * qs, u0.z * qs, u0.w * qs,
-                                    u1.x * qs, u1.y * qs, u1.z * qs, u1.w * qs};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qh[rb][b][e] = (_Float16)x[e];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ql[rb][b][e] = (_Float16)(x[e] - (float)qh[rb][b][e]);
-            }
     }
     // the first key chunk must have landed before the barrier publishes it
     if (key_wave) wait_chunks_after<C::A_LOADS>(min(C::K_PRE - 1, nk - 1));
@@ -758,15 +793,16 @@ void k_attend_mfma(AttendArgs a) {
     __syncthreads();
 
     // Sixteen threads per row, every wave of the workgroup: lane q + 4 a + 16 b of wave w
-    // (q, a, b in 0..3) holds dims FD * (q + 4 b) .. + FD - 1 of row 4 w + a. The FWHT stages
+    // (q, a, b in 0..3) holds dims FD * (q + 4 b) .. + FD - 1 of row 4 w + a (and of the rows
+    // 4 * WAVES further on, while any are left). The FWHT stages
     // below FD run in registers; the four above, partners lane ^ 1 and ^ 2 (a quad
     // permutation, DPP) and lane ^ 16 and ^ 32 (row swaps), across lanes. (The indices are
     // rebuilt from the lane id here rather than kept live, and spilled, across the loop.)
     constexpr int FD = D / 16;
     const int fq = lane & 3, fa = (lane >> 2) & 3, fb = lane >> 4;
     const int ft = fq + 4 * fb;
-    const int row = 4 * w + fa;
-    if (4 * w < ROWS) {
+    for (int row0 = 4 * w; row0 < ROWS; row0 += 4 * C::WAVES) {
+        const int row = row0 + fa;
         float x[FD];
         const int d0 = FD * ft;
         const float* p0 = ob + min(row, ROWS - 1) * MRS + (d0 >> 5) * MQS + (d0 & 31);

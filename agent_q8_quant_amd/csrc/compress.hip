@@ -244,7 +244,8 @@ hipError_t launch_compress_k_range(const void* k_fp16, uint8_t* pool, const Pool
 
 hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
                                    const CodebookHalf& cb, int32_t tok0, int32_t n_tok,
-                                   int32_t layer_begin, int32_t layer_count, hipStream_t s) {
+                                   int32_t layer_begin, int32_t layer_count, hipStream_t s,
+                                   bool valu) {
     TokRange rg;
     rg.tok0 = (uint32_t)tok0;
     rg.n_tok = (uint32_t)n_tok;
@@ -255,6 +256,15 @@ hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const Pool
     const uint32_t blocks = (uint32_t)((waves + 3) / 4);
     const __half* v = (const __half*)v_fp16;
     const uint32_t mblocks = (uint32_t)((items + 3) / 4);  // one wave per 32-token group
+    if (valu) {
+        switch (g.head_dim) {
+            case 64: hipLaunchKernelGGL(k_compress_v<64>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+            case 128: hipLaunchKernelGGL(k_compress_v<128>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+            case 256: hipLaunchKernelGGL(k_compress_v<256>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (g.head_dim) {
         case 64: hipLaunchKernelGGL(k_compress_v_mfma<64>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
         case 128: hipLaunchKernelGGL(k_compress_v_mfma<128>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
@@ -271,8 +281,8 @@ hipError_t launch_compress_k(const void* k_fp16, uint8_t* pool, const PoolGeom& 
 
 hipError_t launch_compress_v(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
                              const CodebookHalf& cb, int32_t layer_begin, int32_t layer_count,
-                             hipStream_t s) {
-    return launch_compress_v_range(v_fp16, pool, g, cb, 0, g.n_tokens, layer_begin, layer_count, s);
+                             hipStream_t s, bool valu) {
+    return launch_compress_v_range(v_fp16, pool, g, cb, 0, g.n_tokens, layer_begin, layer_count, s, valu);
 }
 
 }  // namespace polykv

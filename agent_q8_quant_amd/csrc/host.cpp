@@ -225,17 +225,28 @@ int polykv_compress_k(const void* k_fp16, void* pool, const polykv_layout_t* lay
 int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* layout,
                       const polykv_codebook_t* cb, int32_t layer_begin, int32_t layer_count,
                       void* hip_stream) {
+    return polykv_compress_v_path(v_fp16, pool, layout, cb, layer_begin, layer_count, hip_stream,
+                                  POLYKV_PATH_AUTO);
+}
+
+int polykv_compress_v_path(const void* v_fp16, void* pool, const polykv_layout_t* layout,
+                           const polykv_codebook_t* cb, int32_t layer_begin, int32_t layer_count,
+                           void* hip_stream, int32_t path) {
     if (!v_fp16 || !pool || !layout) return POLYKV_ERR_NULL;
+    if (path < POLYKV_PATH_AUTO || path > POLYKV_PATH_MFMA) return POLYKV_ERR_ARG;
     int rc = check_layout(layout);
     if (rc) return rc;
     if (!aligned(pool, 256) || !aligned(v_fp16, 16)) return POLYKV_ERR_ALIGN;
     if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
     const polykv_codebook_t& book = cb ? *cb : default_codebook();
     if (!codebook_ok(book)) return POLYKV_ERR_CODEBOOK;
+    const bool mfma_ok = layout->shape.head_dim == 64 || layout->shape.head_dim == 128;
+    if (path == POLYKV_PATH_MFMA && !mfma_ok) return POLYKV_ERR_SHAPE;
+    const bool valu = path == POLYKV_PATH_VALU || !mfma_ok;
     if ((rc = check_device())) return rc;
     return launch_rc(polykv::launch_compress_v(v_fp16, (uint8_t*)pool, polykv::make_geom(*layout),
                                                half_of(book), layer_begin, layer_count,
-                                               (hipStream_t)hip_stream));
+                                               (hipStream_t)hip_stream, valu));
 }
 
 static int check_tokens(const polykv_layout_t& l, int32_t token_begin, int32_t n_new) {

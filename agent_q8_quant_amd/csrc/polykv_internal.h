@@ -70,12 +70,15 @@ hipError_t launch_compress_k(const void* k_fp16, uint8_t* pool, const PoolGeom& 
 hipError_t launch_compress_k_range(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
                                    int32_t tok0, int32_t n_tok, int32_t layer_begin,
                                    int32_t layer_count, hipStream_t s);
+// valu: the in-register butterfly kernel for every head_dim (else the matrix-core rotation
+// for head_dim 64 and 128).
 hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
                                    const CodebookHalf& cb, int32_t tok0, int32_t n_tok,
-                                   int32_t layer_begin, int32_t layer_count, hipStream_t s);
+                                   int32_t layer_begin, int32_t layer_count, hipStream_t s,
+                                   bool valu = false);
 hipError_t launch_compress_v(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
                              const CodebookHalf& cb, int32_t layer_begin,
-                             int32_t layer_count, hipStream_t s);
+                             int32_t layer_count, hipStream_t s, bool valu = false);
 
 struct AttendArgs {
     const uint8_t* pool;

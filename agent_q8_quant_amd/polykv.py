@@ -19,6 +19,7 @@ POLYKV_MAX_ROWS = 64
 
 EXPORTED_SYMBOLS = (
     "polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k", "polykv_compress_v",
+    "polykv_compress_v_path",
     "polykv_attend_workspace_bytes", "polykv_attend_path", "polykv_attend_shared", "polykv_attend_shared_path",
     "polykv_attend_shared_lse", "polykv_attend_shared_prefix", "polykv_attend_tail_merge",
     "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v",
@@ -66,6 +67,8 @@ def lib():
         L.polykv_compress_k.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t), i32, i32, vp]
         L.polykv_compress_v.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t),
                                         ctypes.POINTER(polykv_codebook_t), i32, i32, vp]
+        L.polykv_compress_v_path.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t),
+                                             ctypes.POINTER(polykv_codebook_t), i32, i32, vp, i32]
         L.polykv_dequant_k.argtypes = [vp, ctypes.POINTER(polykv_layout_t), vp, i32, i32, vp]
         L.polykv_project_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
         L.polykv_project_compress.argtypes = [vp, vp, vp, vp, ctypes.POINTER(polykv_layout_t),
@@ -90,7 +93,7 @@ def lib():
         L.polykv_strerror.argtypes = [ctypes.c_int]
         L.polykv_strerror.restype = ctypes.c_char_p
         for name in ("polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k",
-                     "polykv_compress_v", "polykv_attend_shared", "polykv_attend_shared_path",
+                     "polykv_compress_v", "polykv_compress_v_path", "polykv_attend_shared", "polykv_attend_shared_path",
                      "polykv_attend_shared_lse", "polykv_attend_shared_prefix", "polykv_attend_tail_merge",
                      "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v",
                      "polykv_project_kv", "polykv_project_compress"):
@@ -155,14 +158,16 @@ def polykv_compress_k(k, pool, layout, layer_begin=0, layer_count=None, stream=N
     _check(rc, "polykv_compress_k")
 
 
-def polykv_compress_v(v, pool, layout, cb=None, layer_begin=0, layer_count=None, stream=None):
+def polykv_compress_v(v, pool, layout, cb=None, layer_begin=0, layer_count=None, stream=None,
+                      path=POLYKV_PATH_AUTO):
+    """Compress v [layer_count][H][T][d] into the pool; path picks the rotation kernel."""
     lb, lc = _layers(layout, layer_begin, layer_count)
     if v.numel() != _kv_elems(layout, lc) or pool.numel() < layout.total_bytes:
         raise ValueError("v or pool has the wrong size for the layout")
-    rc = lib().polykv_compress_v(_dev(v, torch.float16, "v"), _dev(pool, torch.uint8, "pool"),
-                                 ctypes.byref(layout), ctypes.byref(cb) if cb is not None else None,
-                                 lb, lc, _stream_ptr(stream))
-    _check(rc, "polykv_compress_v")
+    rc = lib().polykv_compress_v_path(_dev(v, torch.float16, "v"), _dev(pool, torch.uint8, "pool"),
+                                      ctypes.byref(layout), ctypes.byref(cb) if cb is not None else None,
+                                      lb, lc, _stream_ptr(stream), int(path))
+    _check(rc, "polykv_compress_v_path")
 
 
 def _append_size(layout, t, n_new, lc, name):

@@ -49,10 +49,39 @@ def _parse():
     p.add_argument("--tail-tokens", type=int, default=None,
                    help="private fp16 tail per agent for the tail-merge figure (default: the decode steps)")
     p.add_argument("--cpu-sample-layers", type=int, default=None)
-    p.add_argument("--mode", choices=["bench", "profile", "copy"], default="bench",
+    p.add_argument("--mode", choices=["bench", "profile", "copy", "summarize"], default="bench",
                    help="profile: a few launches for rocprofv3 and no JSON; copy: a 1 GiB device copy "
-                        "for counter calibration")
+                        "for counter calibration; summarize: write profiles/ from rocprofv3 output")
+    # summarize: rocprofv3 output directories and the exact commands that produced them
+    p.add_argument("--trace-dir")
+    p.add_argument("--trace-cmd", default="")
+    p.add_argument("--fetch-dir")
+    p.add_argument("--fetch-cmd", default="")
+    p.add_argument("--write-dir")
+    p.add_argument("--write-cmd", default="")
+    p.add_argument("--calib-fetch-dir")
+    p.add_argument("--calib-write-dir")
+    p.add_argument("--calib-cmds", default="")
+    p.add_argument("--workload", help="workload name the summaries are filed under")
+    p.add_argument("--only", default="", help="comma-separated profile names to write (default: all found)")
     return p.parse_args()
+
+
+# Product kernels as they appear in rocprofv3 traces: (profile name, part of the demangled
+# kernel name, the source files its code comes from).
+KERNELS = (
+    ("attend_mfma", "k_attend_mfma<", ("attend_mfma.hip", "lds_dma.h", "polykv_internal.h")),
+    ("attend_valu", "k_attend_valu<", ("attend.hip", "polykv_internal.h")),
+    ("attend_tail", "k_attend_tail<", ("attend_tail.hip", "polykv_internal.h")),
+    ("compress_k", "k_compress_k", ("compress.hip", "codec.h", "polykv_internal.h")),
+    ("compress_v", "k_compress_v_mfma<", ("compress.hip", "codec.h", "polykv_internal.h")),
+    ("compress_v_valu", "k_compress_v<", ("compress.hip", "codec.h", "polykv_internal.h")),
+    ("dequant_k", "k_dequant_k", ("dequant.hip", "polykv_internal.h")),
+    ("dequant_v", "k_dequant_v<", ("dequant.hip", "polykv_internal.h")),
+    ("project_store", ", 0>(polykv::(anonymous namespace)::PjArgs)", ("project.hip", "codec.h", "lds_dma.h", "polykv_internal.h")),
+    ("project_pool", ", 1>(polykv::(anonymous namespace)::PjArgs)", ("project.hip", "codec.h", "lds_dma.h", "polykv_internal.h")),
+)
+SOURCES = {name: files for name, _, files in KERNELS}
 
 
 def _src_sha(names):
@@ -63,18 +92,133 @@ def _src_sha(names):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel, src_names, workload):
+def _traffic(kernel, workload):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    sha = _src_sha(src_names)
+    sha = _src_sha(SOURCES[kernel])
     for line in open(path):
         f = line.split()
         if len(f) == 4 and not line.startswith("#") and f[0] == kernel and f[1] == workload:
             return int(f[3]) if f[2] == sha else None
     return None
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit("no %s under %s" % (suffix, d))
+    return list(csv.DictReader(open(files[0])))
+
+
+def _kernel_of(name):
+    for prof, key, _ in KERNELS:
+        if key in name and "polykv" in name:
+            return prof
+    return None
+
+
+def _counter(d, counter):
+    """{profile name: {grid: [per-dispatch value]}} of one PMC counter."""
+    out = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        prof = _kernel_of(r["Kernel_Name"])
+        if prof:
+            out.setdefault(prof, {}).setdefault(r["Grid_Size"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            out[prof][r["Grid_Size"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: {g: list(v.values()) for g, v in gr.items()} for k, gr in out.items()}
+
+
+def summarize(args):
+    """Write profiles/<kernel>_<workload>.txt and profiles/hbm_traffic.txt from rocprofv3
+    output: kernel-trace durations per launch grid, and FETCH_SIZE / WRITE_SIZE per dispatch
+    scaled by what the same counters read for a 1 GiB device copy. Every figure written here
+    comes from the given directories; the source hash is computed from the current files."""
+    import statistics
+    wl = args.workload
+    prof_dir = os.path.join(ROOT, "profiles")
+    fscale = wscale = None
+    if args.calib_fetch_dir and args.calib_write_dir:
+        cf = [float(r["Counter_Value"]) for r in _csv_rows(args.calib_fetch_dir, "counter_collection.csv")
+              if r["Counter_Name"] == "FETCH_SIZE" and "copyBuffer" in r["Kernel_Name"]]
+        cw = [float(r["Counter_Value"]) for r in _csv_rows(args.calib_write_dir, "counter_collection.csv")
+              if r["Counter_Name"] == "WRITE_SIZE" and "copyBuffer" in r["Kernel_Name"]]
+        kib = float(1 << 20)  # 1 GiB in KiB
+        fscale, wscale = kib / statistics.mean(cf), kib / statistics.mean(cw)
+        with open(os.path.join(prof_dir, "hbm_counter_calibration_copy_1GiB.txt"), "w") as f:
+            f.write("# HBM counter calibration: 1 GiB device-to-device copy\n\n")
+            f.write("Commands (repository root, one MI355X):\n%s\n\n" % args.calib_cmds)
+            f.write("Kernel __amd_rocclr_copyBuffer, 1 GiB read + 1 GiB written per dispatch, %d dispatches.\n" % len(cf))
+            f.write("FETCH_SIZE per dispatch: %.0f KiB -> scale %.4f (1048576 KiB actually read)\n" % (statistics.mean(cf), fscale))
+            f.write("WRITE_SIZE per dispatch: %.0f KiB -> scale %.4f (1048576 KiB actually written)\n" % (statistics.mean(cw), wscale))
+    else:
+        for line in open(os.path.join(prof_dir, "hbm_counter_calibration_copy_1GiB.txt")):
+            if line.startswith("FETCH_SIZE per dispatch"):
+                fscale = float(line.split("scale")[1].split()[0])
+            if line.startswith("WRITE_SIZE per dispatch"):
+                wscale = float(line.split("scale")[1].split()[0])
+    trace = {}
+    names = {}
+    for r in _csv_rows(args.trace_dir, "kernel_trace.csv"):
+        prof = _kernel_of(r["Kernel_Name"])
+        if not prof:
+            continue
+        g = "%s x %s x %s" % (r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"])
+        trace.setdefault(prof, {}).setdefault(g, []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+        names[prof] = r["Kernel_Name"]
+    fetch = _counter(args.fetch_dir, "FETCH_SIZE") if args.fetch_dir else {}
+    write = _counter(args.write_dir, "WRITE_SIZE") if args.write_dir else {}
+    only = set(filter(None, args.only.split(",")))
+    traffic_path = os.path.join(prof_dir, "hbm_traffic.txt")
+    table = {}
+    if os.path.exists(traffic_path):
+        for line in open(traffic_path):
+            f = line.split()
+            if len(f) == 4 and not line.startswith("#") and f[0] in SOURCES:
+                table[(f[0], f[1])] = line.rstrip("\n")
+    for prof in sorted(trace):
+        if only and prof not in only:
+            continue
+        sha = _src_sha(SOURCES[prof])
+        lines = ["# %s on %s (rocprofv3, one MI355X)" % (prof, wl), "",
+                 "Kernel: %s" % names[prof],
+                 "Source: %s under agent_q8_quant_amd/csrc (sha256 prefix %s)" % (", ".join(SOURCES[prof]), sha), "",
+                 "## Kernel trace (durations, per launch grid)",
+                 "Command (repository root):", "  " + args.trace_cmd]
+        for g, d in sorted(trace[prof].items(), key=lambda kv: -len(kv[1])):
+            sd = statistics.pstdev(d) if len(d) > 1 else 0.0
+            lines.append("grid %s: calls %d, average %.2f us, median %.2f us, min %.2f us, max %.2f us, std %.2f us"
+                         % (g, len(d), statistics.mean(d), statistics.median(d), min(d), max(d), sd))
+        if prof in fetch and prof in write:
+            # the grid launched most often in the counter runs is the workload-sized one
+            gf = max(fetch[prof], key=lambda g: len(fetch[prof][g]))
+            gw = max(write[prof], key=lambda g: len(write[prof][g]))
+            fk, wk = statistics.mean(fetch[prof][gf]), statistics.mean(write[prof][gw])
+            total = int(round(fk * 1024 * fscale + wk * 1024 * wscale))
+            lines += ["", "## HBM traffic per dispatch (PMC, one counter per run; grid size %s)" % gf,
+                      "Commands (repository root):", "  " + args.fetch_cmd, "  " + args.write_cmd,
+                      "FETCH_SIZE %.0f KiB raw x %.4f = %.2f MB read   (%d dispatches)" % (fk, fscale, fk * 1024 * fscale / 1e6, len(fetch[prof][gf])),
+                      "WRITE_SIZE %.0f KiB raw x %.4f = %.2f MB written (%d dispatches)" % (wk, wscale, wk * 1024 * wscale / 1e6, len(write[prof][gw])),
+                      "Total HBM bytes per dispatch: %d" % total,
+                      "Scales from hbm_counter_calibration_copy_1GiB.txt."]
+            key = (prof, wl if prof != "attend_tail" else wl + "_tail%s" % args.tail_tokens)
+            table[key] = "%s %s %s %d" % (key[0], key[1], sha, total)
+        name = "%s_%s.txt" % (prof, wl)
+        with open(os.path.join(prof_dir, name), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("wrote profiles/%s" % name)
+    with open(traffic_path, "w") as f:
+        f.write("# kernel workload source_sha256_prefix hbm_bytes_per_dispatch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)\n")
+        for k in sorted(table):
+            f.write(table[k] + "\n")
+    print("wrote profiles/hbm_traffic.txt")
 
 
 def cpu_baseline(cfg, n_layers_sample, n_steps_sample):
@@ -131,6 +275,9 @@ def _analytic(cfg):
 
 def main():
     args = _parse()
+    if args.mode == "summarize":
+        summarize(args)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(the pool would shard by KV head with no collective; see DESIGN.md)", file=sys.stderr)
@@ -274,6 +421,9 @@ def main():
             # compress kernels' statistics stay those of the one-shot compress)
             if proj is not None:
                 project_fused(0)
+            if cfg.head_dim in (64, 128):
+                for i in range(2 * n_pools):
+                    pk.polykv_compress_v(v, pools[i % n_pools], lay, stream=stream, path=pk.POLYKV_PATH_VALU)
             for i in range(2 * n_pools):
                 dequant(i, "k")
                 dequant(i, "v")
@@ -319,6 +469,21 @@ def main():
                 e1 = ev()
                 if i >= n_pools:
                     tail_ev.append((e0, e1))
+            stream.synchronize()
+
+        # Secondary figure: the value compress with the rotation on the vector ALU instead of
+        # the matrix cores (the same pool bytes up to boundary codes), for the kernel choice.
+        cvv_ev = []
+        if cfg.head_dim in (64, 128):
+            for i in range(n_pools + 6):
+                e0 = ev()
+                pk.polykv_compress_v(v, pools[i % n_pools], lay, stream=stream, path=pk.POLYKV_PATH_VALU)
+                e1 = ev()
+                if i >= n_pools:
+                    cvv_ev.append((e0, e1))
+            stream.synchronize()
+            for i in range(n_pools):  # the pools hold the matrix-core compress again
+                pk.polykv_compress_v(v, pools[i], lay, stream=stream)
             stream.synchronize()
 
         # Secondary figure: the same compression as prefill chunks appended one at a time.
@@ -389,9 +554,8 @@ def main():
     decode_gbps = decode_bytes / t_at / 1e9
     workload = cfg.name
     chosen = pk.polykv_attend_path(lay, cfg.n_agents, cfg.gqa) if path == pk.POLYKV_PATH_AUTO else path
-    kname, ksrc = (("attend_mfma", "attend_mfma.hip") if chosen == pk.POLYKV_PATH_MFMA
-                   else ("attend_valu", "attend.hip"))
-    traffic = _traffic(kname, [ksrc], workload)
+    kname = "attend_mfma" if chosen == pk.POLYKV_PATH_MFMA else "attend_valu"
+    traffic = _traffic(kname, workload)
     result = {
         "metric": METRIC,
         "value": cfg.n_agents * D / step_s,
@@ -433,7 +597,14 @@ def main():
                                 "us": t_tail * 1e6, "GBps": tail_bytes / t_tail / 1e9,
                                 "frac_hbm": tail_bytes / t_tail / 1e9 / HBM_PEAK_GBPS,
                                 "algorithmic_bytes_per_launch": tail_bytes,
-                                "traffic": _traffic("attend_tail", ["attend_tail.hip"], "%s_tail%d" % (workload, n_tail))}
+                                "traffic": _traffic("attend_tail", "%s_tail%d" % (workload, n_tail))}
+    if cvv_ev:
+        t_vv = sum(a.elapsed_time(b) for a, b in cvv_ev) / len(cvv_ev) / 1e3
+        vbytes = fp16_bytes + cfg.kv_elems * 3 // 8 + cfg.n_layers * cfg.n_kv_heads * cfg.n_tokens * 2
+        result["compress_v_vector_alu"] = {
+            "kernel": "compress_v (rotation on the vector ALU)", "us": t_vv * 1e6,
+            "GBps": vbytes / t_vv / 1e9, "frac_hbm": vbytes / t_vv / 1e9 / HBM_PEAK_GBPS,
+            "vs_matrix_core_us": t_cv * 1e6}
     t_app = sum(a.elapsed_time(b) for a, b in app_ev) / len(app_ev) / 1e3
     result["append"] = {"kernels": ["compress_k", "compress_v"], "chunk_tokens": chunk,
                         "chunks": len(chunks), "us": t_app * 1e6,
@@ -460,8 +631,7 @@ def main():
         "GBps": {"k": dk_bytes / t_dk / 1e9, "v": dv_bytes / t_dv / 1e9},
         "frac_hbm": {"k": dk_bytes / t_dk / 1e9 / HBM_PEAK_GBPS, "v": dv_bytes / t_dv / 1e9 / HBM_PEAK_GBPS},
         "algorithmic_bytes_per_launch": {"k": dk_bytes, "v": dv_bytes},
-        "traffic": {"k": _traffic("dequant_k", ["dequant.hip"], workload),
-                    "v": _traffic("dequant_v", ["dequant.hip"], workload)}}
+        "traffic": {"k": _traffic("dequant_k", workload), "v": _traffic("dequant_v", workload)}}
     t_cp = sum(a.elapsed_time(b) for a, b in cp_ev) / len(cp_ev) / 1e3
     result["device_copy_reference"] = {
         "what": "torch copy of one pool copy (read + write), sources rotating like the decode",

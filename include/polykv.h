@@ -55,6 +55,11 @@ extern "C" {
 
 #define POLYKV_MAX_ROWS 64         /* agents x query heads per KV head, per pool tile     */
 
+/* Kernel choice for polykv_compress_v_path and polykv_attend_shared_path. */
+#define POLYKV_PATH_AUTO 0   /* matrix cores where supported (head_dim 64/128), else VALU */
+#define POLYKV_PATH_VALU 1   /* vector ALU (fp32)                                         */
+#define POLYKV_PATH_MFMA 2   /* matrix cores (fp16 operands, fp32 accumulation)           */
+
 /* Pool geometry. */
 typedef struct {
     int32_t n_layers;
@@ -135,6 +140,20 @@ int polykv_compress_k(const void* k_fp16, void* pool, const polykv_layout_t* lay
 int polykv_compress_v(const void* v_fp16, void* pool, const polykv_layout_t* layout,
                       const polykv_codebook_t* cb, int32_t layer_begin, int32_t layer_count,
                       void* hip_stream);
+
+/*
+ * As polykv_compress_v with an explicit kernel for the rotation (POLYKV_PATH_*):
+ * POLYKV_PATH_MFMA computes y = H v on the matrix cores (head_dim 64 and 128; the
+ * automatic choice there), POLYKV_PATH_VALU as an in-register butterfly on the vector ALU
+ * (every head_dim; the automatic choice for 256). Both write the same pool bytes up to the
+ * value-code rule at decision boundaries (codes may differ only where y lies within
+ * rounding of a boundary). PolyKV, Abstract: the values are rotated by a fast
+ * Walsh-Hadamard transform before their 3-bit quantisation.
+ * Errors: as polykv_compress_v; SHAPE for MFMA with head_dim 256; ARG for another path.
+ */
+int polykv_compress_v_path(const void* v_fp16, void* pool, const polykv_layout_t* layout,
+                           const polykv_codebook_t* cb, int32_t layer_begin, int32_t layer_count,
+                           void* hip_stream, int32_t path);
 
 /*
  * Chunked (append) compression. PolyKV, Abstract: the pool is written a single time; when
@@ -219,10 +238,6 @@ int polykv_dequant_k(const void* pool, const polykv_layout_t* layout, void* k_fp
 int polykv_dequant_v(const void* pool, const polykv_layout_t* layout, const polykv_codebook_t* cb,
                      void* v_fp16, int32_t layer_begin, int32_t layer_count, void* hip_stream);
 
-/* Decode kernel choice for polykv_attend_shared_path. */
-#define POLYKV_PATH_AUTO 0   /* matrix cores where supported (head_dim 64/128), else VALU */
-#define POLYKV_PATH_VALU 1   /* fp32 vector-ALU contraction                               */
-#define POLYKV_PATH_MFMA 2   /* matrix-core contraction (fp16 operands, fp32 accumulate)  */
 
 /* The decode kernel POLYKV_PATH_AUTO selects for these arguments (POLYKV_PATH_VALU or
  * POLYKV_PATH_MFMA), or a negative error code (NULL, SHAPE, RANGE, LAYOUT). Host only. */

@@ -237,3 +237,29 @@ def test_concurrent_key_and_value_compress(cfg):
         sk.synchronize()
         sv.synchronize()
         assert torch.equal(pool, seq), "round %d" % r
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_vector_alu_value_compress(d):
+    """polykv_compress_v_path with the vector-ALU rotation at head_dim 64 and 128 (the sizes
+    where the matrix-core rotation is the automatic choice): oracle parity by the value
+    rule, and the same pool as the matrix-core path except at boundary coordinates."""
+    L, H, T = 2, 3, 333
+    rng = np.random.default_rng(d + 5)
+    vx = rng.standard_normal((L, H, T, d)).astype(np.float16)
+    vx[0, 1, 7] = 0.0                      # a zero vector
+    vx[1, 2, 11] = np.float16(0.5)         # a constant vector (ties at y = 0)
+    lay = pk.polykv_pool_layout(L, H, d, T)
+    v = torch.from_numpy(vx).to(device())
+    pools = {}
+    for path in (pk.POLYKV_PATH_VALU, pk.POLYKV_PATH_MFMA):
+        pool = new_pool(lay)
+        pk.polykv_compress_v(v, pool, lay, path=path)
+        torch.cuda.synchronize()
+        pools[path] = read_pool(pool, lay)
+    want_codes, want_norms = oracle.tq_mse_encode(vx, B32)
+    want_planes = oracle.pack_v_planes(want_codes).reshape(L * H, -1, 3, d)
+    for path, got in pools.items():
+        m, c = check_v_codes(got["v_planes"], want_planes, vx.reshape(L * H, T, d), T)
+        check_norms(got["v_norms"], want_norms.reshape(L * H, T))
+        _say("  path %d: value-code mismatches %d of %d" % (path, m, c))

@@ -108,6 +108,12 @@ def test_compress_validation(L):
     cb = pk.polykv_codebook_default()
     cb.centroid[0], cb.centroid[1] = cb.centroid[1], cb.centroid[0]
     assert L.polykv_compress_v(A16, A256, lb, ctypes.byref(cb), 0, 2, None) == -8
+    # explicit rotation kernel: an unknown path, and the matrix cores at head_dim 256
+    good = pk.polykv_codebook_default()
+    assert L.polykv_compress_v_path(A16, A256, lb, ctypes.byref(good), 0, 2, None, 3) == -10
+    assert L.polykv_compress_v_path(A16, A256, lb, ctypes.byref(good), 0, 2, None, -1) == -10
+    lay256 = pk.polykv_pool_layout(1, 1, 256, 32)
+    assert L.polykv_compress_v_path(A16, A256, ctypes.byref(lay256), None, 0, 1, None, 2) == -2
 
 
 def _attend(L, lay, n_agents=2, gqa=2, scale=0.1, lb=0, lc=2, ws=None, wsb=0, path=0,
