@@ -66,23 +66,80 @@ __device__ __forceinline__ void put_lane(uint32_t& w, uint32_t x, int lane) {
     asm("v_writelane_b32 %0, %1, %2" : "+v"(w) : "s"(x), "i"(lane));
 }
 
+// Thresholds b_k n (k = 4, 5, 6) a token's rotated coordinates y are compared with:
+// y / n > b  <=>  y > b n for n > 0; n = 0 gives y = 0 and infinite thresholds (every code
+// 3). Tokens outside the encoded range have y = 0 and get thresholds -1: then every plane
+// bit of put_code_words comes out 0 (bits past T must be 0; others are merged back by
+// the caller's keep mask).
+struct VThresh {
+    float t4, t5, t6;
+};
+__device__ __forceinline__ VThresh v_thresholds(float n, bool valid, const CodebookHalf& cb) {
+    const float inv_t = valid ? (n > 0.0f ? 1.0f : INFINITY) : -1.0f;
+    VThresh t;
+    t.t4 = n > 0.0f ? cb.boundary_pos[0] * n : inv_t;
+    t.t5 = n > 0.0f ? cb.boundary_pos[1] * n : inv_t;
+    t.t6 = n > 0.0f ? cb.boundary_pos[2] * n : inv_t;
+    return t;
+}
+
+// Codes of one register of rotated coordinates, one per lane, into the group's plane
+// words. A ballot over the wave is two whole plane words: the low 32 lanes hold dim d_lo of
+// tokens 0..31, the high 32 lanes dim d_hi. Word (p, d) of the group (3 x D words) goes to
+// lane (p D + d) % 64 of wv[(p D + d) / 64]; d_lo and d_hi are constants once unrolled.
+// Codes from four compares (sign and |y| against the three positive thresholds):
+// code = 4 + m for y > 0, 3 - m otherwise, m = c4 + c5 + c6 (thermometer), so
+// bit 2 = sign, bit 1 = c5 xnor sign, bit 0 = (c4 ^ c5 ^ c6) xnor sign
+// (for y < 0 exactly on a boundary this gives the higher code).
+template <int D>
+__device__ __forceinline__ void put_code_words(float yy, const VThresh& t, int d_lo, int d_hi,
+                                               uint32_t (&wv)[3 * D / 64]) {
+    const float ay = fabsf(yy);
+    const uint64_t pos = __ballot(yy > 0.0f);
+    const uint64_t c4 = __ballot(ay > t.t4);
+    const uint64_t c5 = __ballot(ay > t.t5);
+    const uint64_t c6 = __ballot(ay > t.t6);
+    uint64_t pl[3];
+    pl[2] = pos;
+    pl[1] = ~(c5 ^ pos);
+    pl[0] = ~(c4 ^ c5 ^ c6 ^ pos);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        const int w0 = p * D + d_lo, w1 = p * D + d_hi;
+        put_lane(wv[w0 / 64], (uint32_t)pl[p], w0 % 64);
+        put_lane(wv[w1 / 64], (uint32_t)(pl[p] >> 32), w1 % 64);
+    }
+}
+
+// The group's plane words from wv (lane-linear per register); bits in `keep`
+// (wave-uniform) are read back and kept, the others written.
+template <int D>
+__device__ __forceinline__ void store_group_words(uint32_t* words, uint32_t keep,
+                                                  const uint32_t (&wv)[3 * D / 64], int lane) {
+    constexpr int WPL = 3 * D / 64;
+    if (keep) {
+#pragma unroll
+        for (int r = 0; r < WPL; ++r) words[64 * r + lane] = (words[64 * r + lane] & keep) | wv[r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < WPL; ++r) words[64 * r + lane] = wv[r];
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // One 32-token value group on the matrix cores (head_dim 64 or 128), one wave. vb holds
 // the B operand: lane l has token l % 32 of the group, dims 16 kk + 8 (l / 32) .. + 7 in
 // vb[kk] (zeros for tokens not encoded here; valid is false for them). The rotation
 // y = H v runs as v_mfma_f32_32x32x16_f16 with the +-1 Sylvester matrix as the A operand
 // (exact in fp16; accumulation in fp32), so lane l ends up holding token l % 32 at output
-// dims 32 mb + 8 (i / 4) + 4 (l / 32) + i % 4 (register i of block mb). A ballot of one
-// register over the wave is then two whole plane words: the low 32 bits belong to one
-// dim, the high 32 bits to the dim 4 further. Codes come from four compares per register
-// (sign and |y| against the three positive thresholds b * n), plane bits from scalar
-// logic on the ballots, and each word moves to the lane that stores it.
+// dims 32 mb + 8 (i / 4) + 4 (l / 32) + i % 4 (register i of block mb): a ballot of one
+// register covers dims d0 (low half) and d0 + 4 (high half).
 // H[m][k] = (-1)^popcount(m & k); for the A fragment of output block mb and k step kk,
 // lane l holds m = 32 mb + l % 32, k = 16 kk + 8 (l / 32) + e, and the sign factors into
 // (-1)^(popcount(a & b) + (a >> 4) * (kk & 1)) * (-1)^popcount(mb & (kk >> 1)) with
 // a = l % 32 and b = 8 (l / 32) + e.
-// words: the group's 3 x D plane words; bits in `keep` (wave-uniform) are read back and
-// kept, the others written. norms: the tile's norms; token: this lane's token index.
+// words: the group's 3 x D plane words (keep: as in store_group_words). norms: the
+// tile's norms; token: this lane's token index.
 // ---------------------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void encode_v_group(const h8 (&vb)[D / 16], bool valid, const CodebookHalf& cb,
@@ -117,13 +174,7 @@ __device__ __forceinline__ void encode_v_group(const h8 (&vb)[D / 16], bool vali
         ss = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
     const float n = sqrtf(ss);
-    // y / n > b  <=>  y > b n for n > 0; n = 0 gives y = 0 and infinite thresholds (every
-    // code 3). Tokens outside the range have y = 0 and get thresholds -1: then every plane
-    // bit below comes out 0 (bits past T must be 0; others are merged back by keep_mask).
-    const float inv_t = valid ? (n > 0.0f ? 1.0f : INFINITY) : -1.0f;
-    const float t4 = n > 0.0f ? cb.boundary_pos[0] * n : inv_t;
-    const float t5 = n > 0.0f ? cb.boundary_pos[1] * n : inv_t;
-    const float t6 = n > 0.0f ? cb.boundary_pos[2] * n : inv_t;
+    const VThresh t = v_thresholds(n, valid, cb);
 
     uint32_t wv[WPL];
 #pragma unroll
@@ -140,38 +191,12 @@ __device__ __forceinline__ void encode_v_group(const h8 (&vb)[D / 16], bool vali
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float yy = y[i];
-            const float ay = fabsf(yy);
-            const uint64_t pos = __ballot(yy > 0.0f);
-            const uint64_t c4 = __ballot(ay > t4);
-            const uint64_t c5 = __ballot(ay > t5);
-            const uint64_t c6 = __ballot(ay > t6);
-            // code = 4 + m for y > 0, 3 - m otherwise, m = c4 + c5 + c6 (thermometer):
-            // bit 2 = sign, bit 1 = c5 xnor sign, bit 0 = (c4 ^ c5 ^ c6) xnor sign.
-            // (For y < 0 exactly on a boundary this gives the higher code.)
-            uint64_t pl[3];
-            pl[2] = pos;
-            pl[1] = ~(c5 ^ pos);
-            pl[0] = ~(c4 ^ c5 ^ c6 ^ pos);
-            // word (p, d) of the group goes to lane (p D + d) % 64 of register (p D + d) / 64;
-            // the ballot covers dims d0 (low half) and d0 + 4 (high half)
             const int d0 = 32 * mb + 8 * (i / 4) + (i % 4);
-#pragma unroll
-            for (int p = 0; p < 3; ++p) {
-                const int w0 = p * D + d0, w1 = w0 + 4;
-                put_lane(wv[w0 / 64], (uint32_t)pl[p], w0 % 64);
-                put_lane(wv[w1 / 64], (uint32_t)(pl[p] >> 32), w1 % 64);
-            }
+            put_code_words<D>(y[i], t, d0, d0 + 4, wv);
         }
     }
 
-    if (keep) {
-#pragma unroll
-        for (int r = 0; r < WPL; ++r) words[64 * r + lane] = (words[64 * r + lane] & keep) | wv[r];
-    } else {
-#pragma unroll
-        for (int r = 0; r < WPL; ++r) words[64 * r + lane] = wv[r];
-    }
+    store_group_words<D>(words, keep, wv, lane);
     if (hl == 0 && valid) norms[token] = __float2half_rn(n);
 }
 

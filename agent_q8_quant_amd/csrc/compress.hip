@@ -75,52 +75,63 @@ __device__ __forceinline__ uint32_t keep_mask(const TokRange& r, uint32_t grp, u
 }
 
 // ---------------------------------------------------------------------------------------
-// Values. One lane owns one token's whole head vector in registers, so the FWHT runs
-// entirely in registers. A wave covers two groups of 32 tokens ("items"): lanes 0-31 the
-// first, lanes 32-63 the second. The plane words of a coordinate are wave ballots: the
-// low 32 bits belong to the first item, the high 32 bits to the second.
+// Values on the vector ALU (every head_dim): one wave per 32-token group of one tile.
+// Lane l holds token l % 32 of the group and its dims [h D / 2, (h + 1) D / 2), h = l / 32,
+// in registers, so the rotation y = H v is log2(D) - 1 butterfly stages inside each lane
+// (dims i and i + s, s < D / 2) and a last stage across the lane pair l, l ^ 32 (dims i
+// and i + D / 2), in the order s = 1, 2, ..., D / 2 of the Sylvester recursion. A ballot
+// of register j is then the plane words of dims j (low lanes) and j + D / 2 (high lanes),
+// coded and packed by codec::put_code_words.
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_compress_v(const __half* __restrict__ v,
                                                     uint8_t* __restrict__ pool, PoolGeom g,
                                                     CodebookHalf cb, int32_t layer_begin,
                                                     uint32_t n_items, TokRange rg) {
-    constexpr int NW = D / 64;  // coordinates per lane in the word buffer
+    constexpr int DH = D / 2;         // dims per lane
+    constexpr int WPL = 3 * D / 64;   // plane words per lane of the store
     const int lane = threadIdx.x & 63;
-    const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+    // wave-uniform (and known to be so: scalar registers and branches)
+    const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256u + threadIdx.x) >> 6));
+    if (item >= n_items) return;  // whole waves only
     const uint32_t T = (uint32_t)g.n_tokens;
-
-    const uint32_t item = wave * 2u + (uint32_t)(lane >> 5);
     const uint32_t tile_local = item / rg.n_grp;
     const uint32_t grp = rg.g_first + (item - tile_local * rg.n_grp);
-    const uint32_t token = grp * 32u + (uint32_t)(lane & 31);
-    const bool valid = item < n_items && token >= rg.tok0 && token < rg.tok0 + rg.n_tok;
+    const uint32_t token = grp * 32u + (uint32_t)l32;
+    const bool valid = token >= rg.tok0 && token < rg.tok0 + rg.n_tok;
 
-    float x[D];
+    float x[DH];
     if (valid) {
-        const uint4* src = reinterpret_cast<const uint4*>(v + ((size_t)tile_local * rg.n_tok + (token - rg.tok0)) * D);
+        const uint4* src = reinterpret_cast<const uint4*>(v + ((size_t)tile_local * rg.n_tok + (token - rg.tok0)) * D + hl * DH);
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            uint4 r = src[c];
+        for (int c = 0; c < DH / 8; ++c) {
+            const uint4 r = src[c];
             const __half* h = reinterpret_cast<const __half*>(&r);
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[8 * c + e] = __half2float(h[e]);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < D; ++i) x[i] = 0.0f;
+        for (int i = 0; i < DH; ++i) x[i] = 0.0f;
     }
 
     float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < D; ++i) ss = fmaf(x[i], x[i], ss);
+    for (int i = 0; i < DH; ++i) ss = fmaf(x[i], x[i], ss);
+    {
+        const uint32_t u = __float_as_uint(ss);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        ss = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     const float n = sqrtf(ss);
 
-    // unnormalised Sylvester FWHT: y = H v
+    // unnormalised Sylvester FWHT: the stages inside the lane, then the one across the pair
+    // (the low lane keeps a + b, the high lane a - b, a the low lane's value)
 #pragma unroll
-    for (int h = 1; h < D; h <<= 1) {
+    for (int h = 1; h < DH; h <<= 1) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
+        for (int i = 0; i < DH; ++i) {
             if (!(i & h)) {
                 const float a = x[i], b = x[i + h];
                 x[i] = a + b;
@@ -128,67 +139,28 @@ __global__ __launch_bounds__(256) void k_compress_v(const __half* __restrict__ v
             }
         }
     }
-
-    // y / n > b  <=>  y > b * n for n > 0. For n = 0 the rotated vector is 0 by definition:
-    // infinite magnitude thresholds make every coordinate code 3.
-    const float t4 = n > 0.0f ? cb.boundary_pos[0] * n : INFINITY;
-    const float t5 = n > 0.0f ? cb.boundary_pos[1] * n : INFINITY;
-    const float t6 = n > 0.0f ? cb.boundary_pos[2] * n : INFINITY;
-
-    uint32_t wlo[3][NW], whi[3][NW];
 #pragma unroll
-    for (int p = 0; p < 3; ++p)
-#pragma unroll
-        for (int c = 0; c < NW; ++c) wlo[p][c] = whi[p][c] = 0u;
-
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-        const float y = x[i];
-        const float a = fabsf(y);
-        int code;
-        if (y > 0.0f) {
-            code = 4 + (a > t4) + (a > t5) + (a > t6);
-        } else {
-            // y > -t  <=>  |y| < t for y <= 0
-            code = (a < t4) + (a < t5) + (a < t6);
-        }
-        const uint64_t m0 = __ballot(valid && (code & 1));
-        const uint64_t m1 = __ballot(valid && (code & 2));
-        const uint64_t m2 = __ballot(valid && (code & 4));
-        if (lane == (i & 63)) {
-            wlo[0][i >> 6] = (uint32_t)m0;
-            wlo[1][i >> 6] = (uint32_t)m1;
-            wlo[2][i >> 6] = (uint32_t)m2;
-            whi[0][i >> 6] = (uint32_t)(m0 >> 32);
-            whi[1][i >> 6] = (uint32_t)(m1 >> 32);
-            whi[2][i >> 6] = (uint32_t)(m2 >> 32);
-        }
+    for (int i = 0; i < DH; ++i) {
+        const uint32_t u = __float_as_uint(x[i]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        // lane l < 32: sw[0] = own value, sw[1] = partner's; lane l >= 32: the reverse
+        const float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
+        x[i] = hl ? lo - hi : lo + hi;
     }
 
-    // stores: every lane writes the words of its own coordinates for both items
-    const size_t tile_base = (size_t)layer_begin * g.n_kv_heads;
+    const codec::VThresh t = codec::v_thresholds(n, valid, cb);
+    uint32_t wv[WPL];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const uint32_t it = wave * 2u + (uint32_t)half;
-        if (it >= n_items) continue;
-        const uint32_t tl = it / rg.n_grp;
-        const uint32_t gr = rg.g_first + (it - tl * rg.n_grp);
-        const uint32_t keep = keep_mask(rg, gr, T);
-        uint32_t* words = reinterpret_cast<uint32_t*>(pool + g.v_planes_off +
-                                                      (tile_base + tl) * g.v_planes_stride) +
-                          (size_t)gr * 3 * D;
+    for (int r = 0; r < WPL; ++r) wv[r] = 0u;
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-#pragma unroll
-            for (int c = 0; c < NW; ++c) {
-                const uint32_t nw = half ? whi[p][c] : wlo[p][c];
-                uint32_t* dst = &words[p * D + c * 64 + lane];
-                *dst = keep ? ((*dst & keep) | nw) : nw;
-            }
-    }
-    if (valid) {
-        __half* norms = reinterpret_cast<__half*>(pool + g.v_norms_off +
-                                                  (tile_base + tile_local) * g.v_norms_stride);
+    for (int j = 0; j < DH; ++j) codec::put_code_words<D>(x[j], t, j, j + DH, wv);
+
+    const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_local;
+    uint32_t* words = reinterpret_cast<uint32_t*>(pool + g.v_planes_off + tile * g.v_planes_stride) +
+                      (size_t)grp * 3 * D;
+    codec::store_group_words<D>(words, keep_mask(rg, grp, T), wv, lane);
+    if (hl == 0 && valid) {
+        __half* norms = reinterpret_cast<__half*>(pool + g.v_norms_off + tile * g.v_norms_stride);
         norms[token] = __float2half_rn(n);
     }
 }
@@ -252,10 +224,8 @@ hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const Pool
     rg.g_first = (uint32_t)tok0 / 32u;
     rg.n_grp = (uint32_t)(tok0 + n_tok - 1) / 32u - rg.g_first + 1u;
     const uint64_t items = (uint64_t)layer_count * g.n_kv_heads * rg.n_grp;
-    const uint64_t waves = (items + 1) / 2;
-    const uint32_t blocks = (uint32_t)((waves + 3) / 4);
     const __half* v = (const __half*)v_fp16;
-    const uint32_t mblocks = (uint32_t)((items + 3) / 4);  // one wave per 32-token group
+    const uint32_t blocks = (uint32_t)((items + 3) / 4);  // one wave per 32-token group
     if (valu) {
         switch (g.head_dim) {
             case 64: hipLaunchKernelGGL(k_compress_v<64>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
@@ -266,8 +236,8 @@ hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const Pool
         return hipGetLastError();
     }
     switch (g.head_dim) {
-        case 64: hipLaunchKernelGGL(k_compress_v_mfma<64>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
-        case 128: hipLaunchKernelGGL(k_compress_v_mfma<128>, dim3(mblocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+        case 64: hipLaunchKernelGGL(k_compress_v_mfma<64>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+        case 128: hipLaunchKernelGGL(k_compress_v_mfma<128>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
         case 256: hipLaunchKernelGGL(k_compress_v<256>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
         default: return hipErrorInvalidValue;
     }
