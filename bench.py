@@ -64,6 +64,8 @@ def _parse():
     p.add_argument("--calib-cmds", default="")
     p.add_argument("--workload", help="workload name the summaries are filed under")
     p.add_argument("--only", default="", help="comma-separated profile names to write (default: all found)")
+    p.add_argument("--sq-dirs", default="", help="comma-separated rocprofv3 --pmc output directories of SQ counters")
+    p.add_argument("--sq-cmds", default="", help="the commands that made --sq-dirs, one per line")
     return p.parse_args()
 
 
@@ -221,6 +223,72 @@ def summarize(args):
     print("wrote profiles/hbm_traffic.txt")
 
 
+def summarize_sq(args):
+    """profiles/sq_counters_<workload>.txt: per kernel, the mean per dispatch of every SQ
+    counter found in the --sq-dirs runs (the grid launched most often), and the shares
+    derived from them."""
+    import statistics
+    vals = {}
+    for d in filter(None, args.sq_dirs.split(",")):
+        per = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            prof = _kernel_of(r["Kernel_Name"])
+            if not prof:
+                continue
+            key = (prof, r["Counter_Name"], r["Grid_Size"])
+            per.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        grids = {}
+        for (prof, cn, g), dv in per.items():
+            grids.setdefault(prof, {}).setdefault(g, len(dv))
+        for (prof, cn, g), dv in per.items():
+            gbest = max(grids[prof], key=lambda x: grids[prof][x])
+            if g == gbest:
+                vals.setdefault(prof, {})[cn] = statistics.mean(dv.values())
+    if not vals:
+        raise SystemExit("no product kernels in --sq-dirs")
+    counters = sorted({c for v in vals.values() for c in v})
+    lines = ["# SQ counters per dispatch, %s shapes (rocprofv3, one MI355X)" % args.workload, "",
+             "Commands (repository root), one pass each:"]
+    lines += ["  " + c for c in args.sq_cmds.splitlines() if c.strip()]
+    lines += ["", "Each kernel's figures are the mean over its dispatches of the launch grid it ran most",
+              "often. GRBM_GUI_ACTIVE is summed over the 8 XCDs: cycles = GRBM_GUI_ACTIVE / 8.",
+              "Derived: per-wave counts = SQ_INSTS_* / SQ_WAVES; VALU active = SQ_ACTIVE_INST_VALU x 4 /",
+              "(1024 SIMDs x cycles), the wave-cycles spent in vector instructions per SIMD cycle (the",
+              "counter runs per wave, so overlapping waves can take it past 100%); MFMA busy =",
+              "SQ_VALU_MFMA_BUSY_CYCLES / (1024 x cycles); LDS bank-conflict share =",
+              "SQ_LDS_BANK_CONFLICT / (SQ_ACTIVE_INST_LDS + SQ_LDS_BANK_CONFLICT).",
+              "Source hashes: as in the kernel's own summary file of this workload.", ""]
+    derived = ("VALU/wave", "MFMA/wave", "LDS/wave", "SALU/wave", "VALU active", "MFMA busy", "LDS conflict share")
+    lines.append("| kernel | " + " | ".join(derived) + " |")
+    lines.append("|---" * (len(derived) + 1) + "|")
+    for prof in sorted(vals):
+        v = vals[prof]
+        cyc = v.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        waves = v.get("SQ_WAVES", 0.0)
+        def per_wave(c):
+            return "%.0f" % (v[c] / waves) if c in v and waves else "-"
+        def share(x):
+            return "%.0f%%" % (100.0 * x) if x is not None else "-"
+        valu = v["SQ_ACTIVE_INST_VALU"] * 4 / (1024 * cyc) if "SQ_ACTIVE_INST_VALU" in v and cyc else None
+        mfma = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc) if "SQ_VALU_MFMA_BUSY_CYCLES" in v and cyc else None
+        lds = None
+        if "SQ_LDS_BANK_CONFLICT" in v and "SQ_ACTIVE_INST_LDS" in v and v["SQ_ACTIVE_INST_LDS"] + v["SQ_LDS_BANK_CONFLICT"] > 0:
+            lds = v["SQ_LDS_BANK_CONFLICT"] / (v["SQ_ACTIVE_INST_LDS"] + v["SQ_LDS_BANK_CONFLICT"])
+        lines.append("| %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            prof, per_wave("SQ_INSTS_VALU"), per_wave("SQ_INSTS_MFMA"), per_wave("SQ_INSTS_LDS"),
+            per_wave("SQ_INSTS_SALU"), share(valu), share(mfma), share(lds)))
+    lines += ["", "Raw means per dispatch:", "", "| kernel | " + " | ".join(counters) + " |",
+              "|---" * (len(counters) + 1) + "|"]
+    for prof in sorted(vals):
+        lines.append("| %s | " % prof + " | ".join("%.0f" % vals[prof][c] if c in vals[prof] else "-"
+                                                   for c in counters) + " |")
+    name = "sq_counters_%s.txt" % args.workload
+    with open(os.path.join(ROOT, "profiles", name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/%s" % name)
+
+
 def cpu_baseline(cfg, n_layers_sample, n_steps_sample):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -276,7 +344,10 @@ def _analytic(cfg):
 def main():
     args = _parse()
     if args.mode == "summarize":
-        summarize(args)
+        if args.trace_dir:
+            summarize(args)
+        if args.sq_dirs:
+            summarize_sq(args)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -421,6 +492,9 @@ def main():
             # compress kernels' statistics stay those of the one-shot compress)
             if proj is not None:
                 project_fused(0)
+                px, pwk, pwv, kt, vt = proj
+                for l in range(cfg.n_layers):
+                    pk.polykv_project_kv(px, pwk, pwv, kt, vt, cfg.n_kv_heads, cfg.head_dim, stream=stream)
             if cfg.head_dim in (64, 128):
                 for i in range(2 * n_pools):
                     pk.polykv_compress_v(v, pools[i % n_pools], lay, stream=stream, path=pk.POLYKV_PATH_VALU)
