@@ -201,6 +201,76 @@ __global__ __launch_bounds__(256) void k_compress_v_mfma(const __half* __restric
     encode_v_group<D>(vb, valid, cb, words, keep_mask(rg, grp, T), norms, token, lane);
 }
 
+// ---------------------------------------------------------------------------------------
+// Keys and values of the same token range in one launch (head_dim 64 and 128). Wave w takes
+// the 32-token group w / 2 of the range (tile-major, as the value kernels number them):
+// even waves its keys, odd waves its values, so every SIMD holds both kinds and the value
+// waves' vector work overlaps the key waves' memory traffic.
+// Keys: 32 tokens x D entries are 4 D pieces of 8 entries; lane l takes pieces l + 64 i,
+// which keeps every load instruction on 1 KB of contiguous input and every quad of lanes on
+// one 32-entry block (codec::q8_encode8). All of a lane's loads are issued before the first
+// encode. Values: as k_compress_v_mfma.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_compress_kv(const __half* __restrict__ k,
+                                                     const __half* __restrict__ v,
+                                                     uint8_t* __restrict__ pool, PoolGeom g,
+                                                     CodebookHalf cb, int32_t layer_begin,
+                                                     uint32_t n_items, TokRange rg) {
+    constexpr int KK = D / 16;        // k steps of the rotation; also key pieces per lane
+    constexpr int PPT = D / 8;        // 8-entry pieces per token row
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256u + threadIdx.x) >> 6));
+    const uint32_t item = wave >> 1;
+    if (item >= n_items) return;  // whole waves only
+    const uint32_t T = (uint32_t)g.n_tokens;
+    const uint32_t tile_local = item / rg.n_grp;
+    const uint32_t grp = rg.g_first + (item - tile_local * rg.n_grp);
+    const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_local;
+
+    if ((wave & 1u) == 0u) {
+        // keys of the group's tokens in the range
+        const uint4* src = reinterpret_cast<const uint4*>(k + (size_t)tile_local * rg.n_tok * D);
+        uint4 raw[KK];
+#pragma unroll
+        for (int i = 0; i < KK; ++i) {
+            const uint32_t pc = (uint32_t)lane + 64u * i;
+            const uint32_t token = grp * 32u + pc / PPT;
+            const bool ok = token >= rg.tok0 && token < rg.tok0 + rg.n_tok;
+            raw[i] = ok ? src[(size_t)(token - rg.tok0) * PPT + pc % PPT] : make_uint4(0, 0, 0, 0);
+        }
+        uint2* codes = reinterpret_cast<uint2*>(pool + g.k_codes_off + tile * g.k_codes_stride);
+        __half* scales = reinterpret_cast<__half*>(pool + g.k_scales_off + tile * g.k_scales_stride);
+#pragma unroll
+        for (int i = 0; i < KK; ++i) {
+            uint32_t packed[2];
+            const __half s16 = q8_encode8(raw[i], packed);
+            const uint32_t pc = (uint32_t)lane + 64u * i;
+            const uint32_t token = grp * 32u + pc / PPT;
+            if (token >= rg.tok0 && token < rg.tok0 + rg.n_tok) {
+                const size_t piece = (size_t)token * PPT + pc % PPT;
+                codes[piece] = make_uint2(packed[0], packed[1]);
+                if ((lane & 3) == 0) scales[piece >> 2] = s16;
+            }
+        }
+        return;
+    }
+
+    const int l32 = lane & 31, hl = lane >> 5;
+    const uint32_t token = grp * 32u + (uint32_t)l32;
+    const bool valid = token >= rg.tok0 && token < rg.tok0 + rg.n_tok;
+    h8 vb[KK];
+    {
+        const h8* src = reinterpret_cast<const h8*>(v + ((size_t)tile_local * rg.n_tok + (valid ? token - rg.tok0 : 0u)) * D + 8 * hl);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) vb[kk] = valid ? src[2 * kk] : h8{};
+    }
+    uint32_t* words = reinterpret_cast<uint32_t*>(pool + g.v_planes_off + tile * g.v_planes_stride) +
+                      (size_t)grp * 3 * D;
+    __half* norms = reinterpret_cast<__half*>(pool + g.v_norms_off + tile * g.v_norms_stride);
+    encode_v_group<D>(vb, valid, cb, words, keep_mask(rg, grp, T), norms, token, lane);
+}
+
 }  // namespace
 
 hipError_t launch_compress_k_range(const void* k_fp16, uint8_t* pool, const PoolGeom& g,
@@ -239,6 +309,32 @@ hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const Pool
         case 64: hipLaunchKernelGGL(k_compress_v_mfma<64>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
         case 128: hipLaunchKernelGGL(k_compress_v_mfma<128>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
         case 256: hipLaunchKernelGGL(k_compress_v<256>, dim3(blocks), dim3(256), 0, s, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_compress_kv_range(const void* k_fp16, const void* v_fp16, uint8_t* pool,
+                                    const PoolGeom& g, const CodebookHalf& cb, int32_t tok0,
+                                    int32_t n_tok, int32_t layer_begin, int32_t layer_count,
+                                    hipStream_t s) {
+    if (g.head_dim == 256) {  // no matrix-core value kernel: the two launches
+        hipError_t e = launch_compress_k_range(k_fp16, pool, g, tok0, n_tok, layer_begin, layer_count, s);
+        if (e != hipSuccess) return e;
+        return launch_compress_v_range(v_fp16, pool, g, cb, tok0, n_tok, layer_begin, layer_count, s, true);
+    }
+    TokRange rg;
+    rg.tok0 = (uint32_t)tok0;
+    rg.n_tok = (uint32_t)n_tok;
+    rg.g_first = (uint32_t)tok0 / 32u;
+    rg.n_grp = (uint32_t)(tok0 + n_tok - 1) / 32u - rg.g_first + 1u;
+    const uint64_t items = (uint64_t)layer_count * g.n_kv_heads * rg.n_grp;
+    const uint32_t blocks = (uint32_t)((2 * items + 3) / 4);  // two waves per group
+    const __half* k = (const __half*)k_fp16;
+    const __half* v = (const __half*)v_fp16;
+    switch (g.head_dim) {
+        case 64: hipLaunchKernelGGL(k_compress_kv<64>, dim3(blocks), dim3(256), 0, s, k, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
+        case 128: hipLaunchKernelGGL(k_compress_kv<128>, dim3(blocks), dim3(256), 0, s, k, v, pool, g, cb, layer_begin, (uint32_t)items, rg); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

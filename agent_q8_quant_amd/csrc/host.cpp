@@ -287,6 +287,40 @@ int polykv_append_v(const void* v_fp16, void* pool, const polykv_layout_t* layou
                                                      layer_count, (hipStream_t)hip_stream));
 }
 
+static int kv_impl(const void* k_fp16, const void* v_fp16, void* pool, const polykv_layout_t* layout,
+                   const polykv_codebook_t* cb, int32_t token_begin, int32_t n_new,
+                   int32_t layer_begin, int32_t layer_count, void* hip_stream) {
+    if (!k_fp16 || !v_fp16 || !pool || !layout) return POLYKV_ERR_NULL;
+    int rc = check_layout(layout);
+    if (rc) return rc;
+    if (!aligned(pool, 256) || !aligned(k_fp16, 16) || !aligned(v_fp16, 16)) return POLYKV_ERR_ALIGN;
+    if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
+    if ((rc = check_tokens(*layout, token_begin, n_new))) return rc;
+    const polykv_codebook_t& book = cb ? *cb : default_codebook();
+    if (!codebook_ok(book)) return POLYKV_ERR_CODEBOOK;
+    if ((rc = check_device())) return rc;
+    return launch_rc(polykv::launch_compress_kv_range(k_fp16, v_fp16, (uint8_t*)pool,
+                                                      polykv::make_geom(*layout), half_of(book),
+                                                      token_begin, n_new, layer_begin, layer_count,
+                                                      (hipStream_t)hip_stream));
+}
+
+int polykv_compress_kv(const void* k_fp16, const void* v_fp16, void* pool,
+                       const polykv_layout_t* layout, const polykv_codebook_t* cb,
+                       int32_t layer_begin, int32_t layer_count, void* hip_stream) {
+    if (!layout) return POLYKV_ERR_NULL;
+    return kv_impl(k_fp16, v_fp16, pool, layout, cb, 0, layout->shape.n_tokens, layer_begin,
+                   layer_count, hip_stream);
+}
+
+int polykv_append_kv(const void* k_fp16, const void* v_fp16, void* pool,
+                     const polykv_layout_t* layout, const polykv_codebook_t* cb,
+                     int32_t token_begin, int32_t n_new, int32_t layer_begin,
+                     int32_t layer_count, void* hip_stream) {
+    return kv_impl(k_fp16, v_fp16, pool, layout, cb, token_begin, n_new, layer_begin,
+                   layer_count, hip_stream);
+}
+
 static int check_projection(int32_t n_tok, int32_t hidden, int32_t n_heads, int32_t head_dim) {
     // hidden <= 2^22 keeps every per-lane byte offset of a 256-row operand tile in 32 bits
     if (n_tok < 1 || n_heads < 1 || hidden < 64 || hidden % 64 != 0 || hidden > (1 << 22)) return POLYKV_ERR_SHAPE;

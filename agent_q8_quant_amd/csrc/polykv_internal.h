@@ -79,6 +79,12 @@ hipError_t launch_compress_v_range(const void* v_fp16, uint8_t* pool, const Pool
 hipError_t launch_compress_v(const void* v_fp16, uint8_t* pool, const PoolGeom& g,
                              const CodebookHalf& cb, int32_t layer_begin,
                              int32_t layer_count, hipStream_t s, bool valu = false);
+// Keys and values of one token range in one launch (two launches for head_dim 256); the
+// inputs hold that range only, as for the single-kind launchers.
+hipError_t launch_compress_kv_range(const void* k_fp16, const void* v_fp16, uint8_t* pool,
+                                    const PoolGeom& g, const CodebookHalf& cb, int32_t tok0,
+                                    int32_t n_tok, int32_t layer_begin, int32_t layer_count,
+                                    hipStream_t s);
 
 struct AttendArgs {
     const uint8_t* pool;

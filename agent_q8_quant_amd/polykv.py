@@ -22,8 +22,9 @@ EXPORTED_SYMBOLS = (
     "polykv_compress_v_path",
     "polykv_attend_workspace_bytes", "polykv_attend_path", "polykv_attend_shared", "polykv_attend_shared_path",
     "polykv_attend_shared_lse", "polykv_attend_shared_prefix", "polykv_attend_tail_merge",
-    "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v",
-    "polykv_project_kv", "polykv_project_compress", "polykv_strerror",
+    "polykv_append_k", "polykv_append_v", "polykv_compress_kv", "polykv_append_kv",
+    "polykv_dequant_k", "polykv_dequant_v", "polykv_project_kv", "polykv_project_compress",
+    "polykv_strerror",
 )
 
 
@@ -88,6 +89,10 @@ def lib():
         L.polykv_append_k.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t), i32, i32, i32, i32, vp]
         L.polykv_append_v.argtypes = [vp, vp, ctypes.POINTER(polykv_layout_t), ctypes.POINTER(polykv_codebook_t),
                                       i32, i32, i32, i32, vp]
+        L.polykv_compress_kv.argtypes = [vp, vp, vp, ctypes.POINTER(polykv_layout_t),
+                                         ctypes.POINTER(polykv_codebook_t), i32, i32, vp]
+        L.polykv_append_kv.argtypes = [vp, vp, vp, ctypes.POINTER(polykv_layout_t),
+                                       ctypes.POINTER(polykv_codebook_t), i32, i32, i32, i32, vp]
         L.polykv_attend_tail_merge.argtypes = [ctypes.POINTER(polykv_layout_t), vp, vp, vp, vp, vp, vp,
                                                i32, i32, i32, ctypes.c_float, i32, vp]
         L.polykv_strerror.argtypes = [ctypes.c_int]
@@ -95,8 +100,8 @@ def lib():
         for name in ("polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k",
                      "polykv_compress_v", "polykv_compress_v_path", "polykv_attend_shared", "polykv_attend_shared_path",
                      "polykv_attend_shared_lse", "polykv_attend_shared_prefix", "polykv_attend_tail_merge",
-                     "polykv_append_k", "polykv_append_v", "polykv_dequant_k", "polykv_dequant_v",
-                     "polykv_project_kv", "polykv_project_compress"):
+                     "polykv_append_k", "polykv_append_v", "polykv_compress_kv", "polykv_append_kv",
+                     "polykv_dequant_k", "polykv_dequant_v", "polykv_project_kv", "polykv_project_compress"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -200,6 +205,33 @@ def polykv_append_v(v, pool, layout, token_begin, n_new=None, cb=None, layer_beg
                                ctypes.byref(cb) if cb is not None else None, int(token_begin), n_new, lb, lc,
                                _stream_ptr(stream))
     _check(rc, "polykv_append_v")
+
+
+def polykv_compress_kv(k, v, pool, layout, cb=None, layer_begin=0, layer_count=None, stream=None):
+    """Compress k and v [layer_count][H][T][d] into the pool in one call."""
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    if k.numel() != _kv_elems(layout, lc) or v.numel() != _kv_elems(layout, lc) or pool.numel() < layout.total_bytes:
+        raise ValueError("k, v or pool has the wrong size for the layout")
+    rc = lib().polykv_compress_kv(_dev(k, torch.float16, "k"), _dev(v, torch.float16, "v"),
+                                  _dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
+                                  ctypes.byref(cb) if cb is not None else None, lb, lc, _stream_ptr(stream))
+    _check(rc, "polykv_compress_kv")
+
+
+def polykv_append_kv(k, v, pool, layout, token_begin, n_new=None, cb=None, layer_begin=0, layer_count=None,
+                     stream=None):
+    """Compress the chunks k and v [layer_count][H][n_new][d] into tokens [token_begin, +n_new)."""
+    lb, lc = _layers(layout, layer_begin, layer_count)
+    n_new = int(k.shape[-2]) if n_new is None else int(n_new)
+    _append_size(layout, k, n_new, lc, "k")
+    _append_size(layout, v, n_new, lc, "v")
+    if pool.numel() < layout.total_bytes:
+        raise ValueError("pool has the wrong size for the layout")
+    rc = lib().polykv_append_kv(_dev(k, torch.float16, "k"), _dev(v, torch.float16, "v"),
+                                _dev(pool, torch.uint8, "pool"), ctypes.byref(layout),
+                                ctypes.byref(cb) if cb is not None else None, int(token_begin), n_new, lb, lc,
+                                _stream_ptr(stream))
+    _check(rc, "polykv_append_kv")
 
 
 def polykv_project_kv(x, w_k, w_v, k, v, n_heads, head_dim, stream=None):

@@ -77,6 +77,7 @@ KERNELS = (
     ("attend_tail", "k_attend_tail<", ("attend_tail.hip", "polykv_internal.h")),
     ("compress_k", "k_compress_k", ("compress.hip", "codec.h", "polykv_internal.h")),
     ("compress_v", "k_compress_v_mfma<", ("compress.hip", "codec.h", "polykv_internal.h")),
+    ("compress_kv", "k_compress_kv<", ("compress.hip", "codec.h", "polykv_internal.h")),
     ("compress_v_valu", "k_compress_v<", ("compress.hip", "codec.h", "polykv_internal.h")),
     ("dequant_k", "k_dequant_k", ("dequant.hip", "polykv_internal.h")),
     ("dequant_v", "k_dequant_v<", ("dequant.hip", "polykv_internal.h")),
@@ -425,9 +426,7 @@ def main():
         # (nothing of it is left in the 256 MB Infinity Cache); all copies are identical.
         pw = j % n_pools
         e = [ev()]
-        pk.polykv_compress_k(k, pools[pw], lay, stream=stream)
-        e.append(ev())
-        pk.polykv_compress_v(v, pools[pw], lay, stream=stream)
+        pk.polykv_compress_kv(k, v, pools[pw], lay, stream=stream)
         e.append(ev())
         # the D decode launches back to back, one event pair around them: an event between
         # launches would add its own packet's time to every launch
@@ -436,11 +435,14 @@ def main():
         e.append(ev())
         rec.append(e)
 
-    def append_all(i):
+    def append_all(i, fused=True):
         # the whole context, chunk by chunk, into pool copy i (it ends up identical)
         for a, b, kc, vc in chunks:
-            pk.polykv_append_k(kc, pools[i % n_pools], lay, a, stream=stream)
-            pk.polykv_append_v(vc, pools[i % n_pools], lay, a, stream=stream)
+            if fused:
+                pk.polykv_append_kv(kc, vc, pools[i % n_pools], lay, a, stream=stream)
+            else:
+                pk.polykv_append_k(kc, pools[i % n_pools], lay, a, stream=stream)
+                pk.polykv_append_v(vc, pools[i % n_pools], lay, a, stream=stream)
 
     # Fused K/V projection + compression (prefill): one layer's input rows x [T][hidden] and
     # the two projection weights [H*d][hidden], seeded normals (random weights, as no
@@ -488,8 +490,11 @@ def main():
                                             cfg.softmax_scale, path, workspace=ws, stream=stream)
                 for i in range(2 * n_pools):
                     tail_merge(i)
-            # (appends run the compress kernels on smaller ranges: left out here, so that the
-            # compress kernels' statistics stay those of the one-shot compress)
+            # the single-kind compress kernels over the whole pool (appends run them on
+            # smaller ranges: left out here, so that their statistics stay the one-shot ones)
+            for i in range(n_pools + max(1, args.steps)):
+                pk.polykv_compress_k(k, pools[i % n_pools], lay, stream=stream)
+                pk.polykv_compress_v(v, pools[i % n_pools], lay, stream=stream)
             if proj is not None:
                 project_fused(0)
                 px, pwk, pwv, kt, vt = proj
@@ -545,6 +550,19 @@ def main():
                     tail_ev.append((e0, e1))
             stream.synchronize()
 
+        # Secondary figure: keys and values compressed by their own launches, one after the
+        # other (the same pool bytes as the one-launch compress of the timed steps).
+        sep_ev = []
+        for i in range(n_pools + 6):
+            e0 = ev()
+            pk.polykv_compress_k(k, pools[i % n_pools], lay, stream=stream)
+            e1 = ev()
+            pk.polykv_compress_v(v, pools[i % n_pools], lay, stream=stream)
+            e2 = ev()
+            if i >= n_pools:
+                sep_ev.append((e0, e1, e2))
+        stream.synchronize()
+
         # Secondary figure: the value compress with the rotation on the vector ALU instead of
         # the matrix cores (the same pool bytes up to boundary codes), for the kernel choice.
         cvv_ev = []
@@ -560,22 +578,30 @@ def main():
                 pk.polykv_compress_v(v, pools[i], lay, stream=stream)
             stream.synchronize()
 
-        # Secondary figure: the same compression as prefill chunks appended one at a time.
-        app_ev = []
-        for i in range(n_pools + 6):
-            e0 = ev()
-            append_all(i)
-            e1 = ev()
-            if i >= n_pools:
-                app_ev.append((e0, e1))
+        # Secondary figure: the same compression as prefill chunks appended one at a time,
+        # keys and values of a chunk in one launch, and in two.
+        app_ev = {True: [], False: []}
+        for fused in (True, False):
+            for i in range(n_pools + 6):
+                e0 = ev()
+                append_all(i, fused)
+                e1 = ev()
+                if i >= n_pools:
+                    app_ev[fused].append((e0, e1))
         stream.synchronize()
 
         # Secondary figure: the K/V projection of every layer with the compression fused in,
         # against the projection written as fp16 and then appended (the same pool bytes).
         # The pools end up holding the projected cache; nothing after this reads them.
-        pj_ev = {"fused": [], "unfused": []}
+        pj_ev = {"fused": [], "unfused": [], "library": []}
         if proj is not None:
-            for name, fn in (("fused", project_fused), ("unfused", project_unfused)):
+            px, pwk, pwv, _, _ = proj
+            w_t = torch.cat([pwk, pwv]).t().contiguous()   # [hidden][2 H d], a plain 2-D GEMM
+
+            def project_library(i):
+                for l in range(cfg.n_layers):
+                    torch.matmul(px, w_t)
+            for name, fn in (("fused", project_fused), ("unfused", project_unfused), ("library", project_library)):
                 fn(0)
                 for i in range(2):
                     e0 = ev()
@@ -611,20 +637,20 @@ def main():
         del cp_dst
 
     step_ms = [r[0].elapsed_time(r[-1]) for r in rec]
-    ck_ms = [r[0].elapsed_time(r[1]) for r in rec]
-    cv_ms = [r[1].elapsed_time(r[2]) for r in rec]
-    at_ms = [r[2].elapsed_time(r[3]) / D for r in rec]
+    ckv_ms = [r[0].elapsed_time(r[1]) for r in rec]
+    at_ms = [r[1].elapsed_time(r[2]) / D for r in rec]
     step_s = sum(step_ms) / len(step_ms) / 1e3
-    t_ck = sum(ck_ms) / len(ck_ms) / 1e3
-    t_cv = sum(cv_ms) / len(cv_ms) / 1e3
+    t_ckv = sum(ckv_ms) / len(ckv_ms) / 1e3
     t_at = sum(at_ms) / len(at_ms) / 1e3
+    t_ck = sum(a.elapsed_time(b) for a, b, _ in sep_ev) / len(sep_ev) / 1e3
+    t_cv = sum(b.elapsed_time(c) for _, b, c in sep_ev) / len(sep_ev) / 1e3
 
     analytic = lay.analytic_bytes
     fp16_bytes = cfg.kv_elems * 2
     q_bytes = cfg.n_layers * cfg.n_agents * cfg.n_q_heads * cfg.head_dim * 4
     compress_bytes = 2 * fp16_bytes + analytic
     decode_bytes = analytic + 2 * q_bytes
-    compress_gbps = compress_bytes / (t_ck + t_cv) / 1e9
+    compress_gbps = compress_bytes / t_ckv / 1e9
     decode_gbps = decode_bytes / t_at / 1e9
     workload = cfg.name
     chosen = pk.polykv_attend_path(lay, cfg.n_agents, cfg.gqa) if path == pk.POLYKV_PATH_AUTO else path
@@ -653,10 +679,14 @@ def main():
         "decode_agent_tokens_per_s": cfg.n_agents / t_at,
         "decode_GBps": decode_gbps, "decode_frac_hbm": decode_gbps / HBM_PEAK_GBPS,
         "compress_GBps": compress_gbps, "compress_frac_hbm": compress_gbps / HBM_PEAK_GBPS,
-        "compress_us": {"k": t_ck * 1e6, "v": t_cv * 1e6},
-        "compress_GBps_k": (fp16_bytes + cfg.kv_elems + cfg.kv_elems // 16) / t_ck / 1e9,
-        "compress_GBps_v": (fp16_bytes + cfg.kv_elems * 3 // 8
-                            + cfg.n_layers * cfg.n_kv_heads * cfg.n_tokens * 2) / t_cv / 1e9,
+        "compress_us": t_ckv * 1e6,
+        "compress_kernel": "compress_kv (keys and values in one launch)",
+        "compress_separate": {
+            "us": {"k": t_ck * 1e6, "v": t_cv * 1e6},
+            "GBps": {"k": (fp16_bytes + cfg.kv_elems + cfg.kv_elems // 16) / t_ck / 1e9,
+                     "v": (fp16_bytes + cfg.kv_elems * 3 // 8
+                           + cfg.n_layers * cfg.n_kv_heads * cfg.n_tokens * 2) / t_cv / 1e9},
+            "GBps_both": compress_bytes / (t_ck + t_cv) / 1e9},
         "wall_ms_per_step": wall / args.steps * 1e3,
     }
     if cold_us:
@@ -679,12 +709,15 @@ def main():
             "kernel": "compress_v (rotation on the vector ALU)", "us": t_vv * 1e6,
             "GBps": vbytes / t_vv / 1e9, "frac_hbm": vbytes / t_vv / 1e9 / HBM_PEAK_GBPS,
             "vs_matrix_core_us": t_cv * 1e6}
-    t_app = sum(a.elapsed_time(b) for a, b in app_ev) / len(app_ev) / 1e3
-    result["append"] = {"kernels": ["compress_k", "compress_v"], "chunk_tokens": chunk,
+    t_app = sum(a.elapsed_time(b) for a, b in app_ev[True]) / len(app_ev[True]) / 1e3
+    t_app2 = sum(a.elapsed_time(b) for a, b in app_ev[False]) / len(app_ev[False]) / 1e3
+    result["append"] = {"kernels": ["compress_kv"], "chunk_tokens": chunk,
                         "chunks": len(chunks), "us": t_app * 1e6,
                         "GBps": compress_bytes / t_app / 1e9,
                         "frac_hbm": compress_bytes / t_app / 1e9 / HBM_PEAK_GBPS,
-                        "algorithmic_bytes": compress_bytes}
+                        "algorithmic_bytes": compress_bytes,
+                        "separate_launches": {"kernels": ["compress_k", "compress_v"], "us": t_app2 * 1e6,
+                                              "frac_hbm": compress_bytes / t_app2 / 1e9 / HBM_PEAK_GBPS}}
     if pj_ev["fused"]:
         t_f = sum(a.elapsed_time(b) for a, b in pj_ev["fused"]) / len(pj_ev["fused"]) / 1e3
         t_u = sum(a.elapsed_time(b) for a, b in pj_ev["unfused"]) / len(pj_ev["unfused"]) / 1e3
@@ -692,6 +725,7 @@ def main():
         result["project_compress"] = {
             "kernel": "project (fused)", "hidden": hidden, "layers": cfg.n_layers,
             "us_fused": t_f * 1e6, "us_unfused": t_u * 1e6,
+            "us_library_gemm_only": sum(a.elapsed_time(b) for a, b in pj_ev["library"]) / len(pj_ev["library"]) * 1e3,
             "roofline": {"bound": "mfma", "achieved": flops / t_f / 1e12, "peak": 2500.0,
                          "unit": "TFLOP/s", "frac": flops / t_f / 1e12 / 2500.0},
             "flops": flops}

@@ -180,6 +180,26 @@ int polykv_append_v(const void* v_fp16, void* pool, const polykv_layout_t* layou
                     int32_t layer_begin, int32_t layer_count, void* hip_stream);
 
 /*
+ * Keys and values in one call. PolyKV, Abstract: the K and V of the shared context go into
+ * the one pool that is written once; a caller that holds both compresses them together.
+ * polykv_compress_kv writes exactly the bytes of polykv_compress_k followed by
+ * polykv_compress_v, and polykv_append_kv those of polykv_append_k followed by
+ * polykv_append_v, with the same arguments (k_fp16 and v_fp16 as described there; cb:
+ * host pointer or NULL for polykv_codebook_default). For head_dim 64 and 128 one launch
+ * encodes both (the value rotation on the matrix cores, as the automatic choice of
+ * polykv_compress_v_path); for head_dim 256 it is the two launches in stream order.
+ * Errors: NULL, ALIGN, RANGE (layer range; token range for append), LAYOUT, CODEBOOK,
+ *         DEVICE, LAUNCH.
+ */
+int polykv_compress_kv(const void* k_fp16, const void* v_fp16, void* pool,
+                       const polykv_layout_t* layout, const polykv_codebook_t* cb,
+                       int32_t layer_begin, int32_t layer_count, void* hip_stream);
+int polykv_append_kv(const void* k_fp16, const void* v_fp16, void* pool,
+                     const polykv_layout_t* layout, const polykv_codebook_t* cb,
+                     int32_t token_begin, int32_t n_new, int32_t layer_begin,
+                     int32_t layer_count, void* hip_stream);
+
+/*
  * K/V projection of one layer's prefill chunk, with the pool compression fused into its
  * epilogue. PolyKV, Abstract: the shared cache is compressed a single time, as it is
  * written; here that happens where K and V are produced, so they never reach HBM as fp16.

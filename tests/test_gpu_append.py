@@ -35,19 +35,24 @@ def _kv(L, H, T, d, seed):
     return k, v
 
 
-def _append(pool, lay, k, v, a, b):
+def _append(pool, lay, k, v, a, b, fused=False):
     kc = torch.from_numpy(np.ascontiguousarray(k[..., a:b, :])).to(device())
     vc = torch.from_numpy(np.ascontiguousarray(v[..., a:b, :])).to(device())
-    pk.polykv_append_k(kc, pool, lay, a)
-    pk.polykv_append_v(vc, pool, lay, a)
+    if fused:
+        pk.polykv_append_kv(kc, vc, pool, lay, a)
+    else:
+        pk.polykv_append_k(kc, pool, lay, a)
+        pk.polykv_append_v(vc, pool, lay, a)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("order", ["forward", "shuffled"])
 @pytest.mark.parametrize("shape", [(2, 2, 128, 600), (1, 3, 64, 95), (1, 2, 256, 70)],
                          ids=lambda s: "L%dH%dd%dT%d" % s)
-def test_append_equals_one_shot(shape, order):
+def test_append_equals_one_shot(shape, order, fused):
+    """fused: the chunks go in through polykv_append_kv (keys and values in one launch)."""
     L, H, d, T = shape
-    print("append", shape, order, flush=True)
+    print("append", shape, order, fused, flush=True)
     k, v = _kv(L, H, T, d, seed=T)
     lay = pk.polykv_pool_layout(L, H, d, T)
     one = new_pool(lay, fill=0x00)
@@ -59,7 +64,7 @@ def test_append_equals_one_shot(shape, order):
         chunks = chunks[::2][::-1] + chunks[1::2]
     app = new_pool(lay, fill=0xA5)
     for a, b in chunks:
-        _append(app, lay, k, v, a, b)
+        _append(app, lay, k, v, a, b, fused)
     torch.cuda.synchronize()
     got, want = _payload(app, lay), _payload(one, lay)
     for key in want:
@@ -73,6 +78,29 @@ def test_append_equals_one_shot(shape, order):
     assert np.array_equal(got["k_codes"].reshape(op["k_codes"].shape), op["k_codes"])
     assert np.array_equal(got["k_scales"].view(np.uint16).reshape(op["k_scales"].shape),
                           op["k_scales"].view(np.uint16))
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 128, 333), (3, 2, 64, 600), (1, 2, 256, 70), (1, 1, 128, 1),
+                                   (32, 8, 128, 256)], ids=lambda s: "L%dH%dd%dT%d" % s)
+def test_fused_compress_equals_separate(shape):
+    """polykv_compress_kv writes the bytes of polykv_compress_k + polykv_compress_v, over
+    the whole allocation (padding included), on layers [1, L) of a pool whose layer 0
+    holds other bytes."""
+    L, H, d, T = shape
+    print("fused compress", shape, flush=True)
+    k, v = _kv(L, H, T, d, seed=7 * T + d)
+    k[0, 0, 0] = 0.0                                  # a zero key block and value vector
+    v[0, 0, 0] = 0.0
+    lay = pk.polykv_pool_layout(L, H, d, T)
+    lb, lc = (1, L - 1) if L > 1 else (0, 1)
+    kk = torch.from_numpy(np.ascontiguousarray(k[lb:lb + lc])).to(device())
+    vv = torch.from_numpy(np.ascontiguousarray(v[lb:lb + lc])).to(device())
+    sep, fus = new_pool(lay, fill=0x5A), new_pool(lay, fill=0x5A)
+    pk.polykv_compress_k(kk, sep, lay, layer_begin=lb, layer_count=lc)
+    pk.polykv_compress_v(vv, sep, lay, layer_begin=lb, layer_count=lc)
+    pk.polykv_compress_kv(kk, vv, fus, lay, layer_begin=lb, layer_count=lc)
+    torch.cuda.synchronize()
+    assert torch.equal(sep, fus)
 
 
 def test_append_writes_only_its_tokens():

@@ -225,6 +225,39 @@ def test_append_and_prefix_validation(L):
                                              ctypes.c_float(0.1), 0, 2, None, 0, None, 0) == -4
 
 
+def test_fused_key_value_validation(L):
+    lay = _layout()
+    lb = ctypes.byref(lay)
+    T = lay.shape.n_tokens
+    unaligned = ctypes.c_void_p(0x20010)
+
+    def comp(k=A16, v=A16, pool=A256, lbeg=0, lc=2, cb=None):
+        return L.polykv_compress_kv(k, v, pool, lb, cb, lbeg, lc, None)
+
+    def app(tb, n, k=A16, v=A16, pool=A256, lbeg=0, lc=2, cb=None):
+        return L.polykv_append_kv(k, v, pool, lb, cb, tb, n, lbeg, lc, None)
+
+    for f in (comp, lambda **a: app(0, 1, **a)):
+        assert f(k=None) == -1
+        assert f(v=None) == -1
+        assert f(pool=None) == -1
+        assert f(pool=unaligned) == -3
+        assert f(v=ctypes.c_void_p(0x10008)) == -3
+        assert f(lbeg=1) == -4               # layer range past the pool
+        assert f(lc=0) == -4
+    assert L.polykv_compress_kv(A16, A16, A256, None, None, 0, 2, None) == -1
+    assert app(-1, 2) == -4
+    assert app(0, 0) == -4
+    assert app(T - 3, 4) == -4
+    cb = pk.polykv_codebook_default()
+    cb.boundary[3] = 0.1
+    assert comp(cb=ctypes.byref(cb)) == -8
+    assert app(0, 1, cb=ctypes.byref(cb)) == -8
+    bad = _layout()
+    bad.total_bytes += 256
+    assert L.polykv_compress_kv(A16, A16, A256, ctypes.byref(bad), None, 0, 2, None) == -9
+
+
 def test_projection_validation(L):
     lay = _layout()
     lb = ctypes.byref(lay)
