@@ -435,14 +435,28 @@ def main():
         e.append(ev())
         rec.append(e)
 
-    def append_all(i, fused=True):
-        # the whole context, chunk by chunk, into pool copy i (it ends up identical)
-        for a, b, kc, vc in chunks:
+    stream2 = torch.cuda.Stream(device=dev)
+
+    def append_all(i, fused=True, two_streams=False):
+        # The whole context, chunk by chunk, into pool copy i (it ends up identical). Chunk
+        # boundaries are multiples of 32 tokens, so consecutive chunks touch disjoint plane
+        # groups and may run concurrently: with two_streams the odd chunks go to a second
+        # stream, joined to the first before and after.
+        if two_streams:
+            e = torch.cuda.Event()
+            e.record(stream)
+            stream2.wait_event(e)
+        for n, (a, b, kc, vc) in enumerate(chunks):
+            st = stream2 if (two_streams and n % 2) else stream
             if fused:
-                pk.polykv_append_kv(kc, vc, pools[i % n_pools], lay, a, stream=stream)
+                pk.polykv_append_kv(kc, vc, pools[i % n_pools], lay, a, stream=st)
             else:
-                pk.polykv_append_k(kc, pools[i % n_pools], lay, a, stream=stream)
-                pk.polykv_append_v(vc, pools[i % n_pools], lay, a, stream=stream)
+                pk.polykv_append_k(kc, pools[i % n_pools], lay, a, stream=st)
+                pk.polykv_append_v(vc, pools[i % n_pools], lay, a, stream=st)
+        if two_streams:
+            e = torch.cuda.Event()
+            e.record(stream2)
+            stream.wait_event(e)
 
     # Fused K/V projection + compression (prefill): one layer's input rows x [T][hidden] and
     # the two projection weights [H*d][hidden], seeded normals (random weights, as no
@@ -578,17 +592,18 @@ def main():
                 pk.polykv_compress_v(v, pools[i], lay, stream=stream)
             stream.synchronize()
 
-        # Secondary figure: the same compression as prefill chunks appended one at a time,
-        # keys and values of a chunk in one launch, and in two.
-        app_ev = {True: [], False: []}
-        for fused in (True, False):
+        # Secondary figure: the same compression as prefill chunks appended one at a time:
+        # keys and values of a chunk in one launch, the chunks alternating over two streams;
+        # the same on one stream; and keys and values in two launches on one stream.
+        app_ev = {"two": [], "one": [], "separate": []}
+        for name, fused, two in (("two", True, True), ("one", True, False), ("separate", False, False)):
             for i in range(n_pools + 6):
                 e0 = ev()
-                append_all(i, fused)
+                append_all(i, fused, two)
                 e1 = ev()
                 if i >= n_pools:
-                    app_ev[fused].append((e0, e1))
-        stream.synchronize()
+                    app_ev[name].append((e0, e1))
+        torch.cuda.synchronize()
 
         # Secondary figure: the K/V projection of every layer with the compression fused in,
         # against the projection written as fp16 and then appended (the same pool bytes).
@@ -709,15 +724,17 @@ def main():
             "kernel": "compress_v (rotation on the vector ALU)", "us": t_vv * 1e6,
             "GBps": vbytes / t_vv / 1e9, "frac_hbm": vbytes / t_vv / 1e9 / HBM_PEAK_GBPS,
             "vs_matrix_core_us": t_cv * 1e6}
-    t_app = sum(a.elapsed_time(b) for a, b in app_ev[True]) / len(app_ev[True]) / 1e3
-    t_app2 = sum(a.elapsed_time(b) for a, b in app_ev[False]) / len(app_ev[False]) / 1e3
-    result["append"] = {"kernels": ["compress_kv"], "chunk_tokens": chunk,
-                        "chunks": len(chunks), "us": t_app * 1e6,
-                        "GBps": compress_bytes / t_app / 1e9,
-                        "frac_hbm": compress_bytes / t_app / 1e9 / HBM_PEAK_GBPS,
+    t_app = {n: sum(a.elapsed_time(b) for a, b in ev_) / len(ev_) / 1e3 for n, ev_ in app_ev.items()}
+    result["append"] = {"kernels": ["compress_kv"], "chunk_tokens": chunk, "chunks": len(chunks),
+                        "streams": 2, "us": t_app["two"] * 1e6,
+                        "GBps": compress_bytes / t_app["two"] / 1e9,
+                        "frac_hbm": compress_bytes / t_app["two"] / 1e9 / HBM_PEAK_GBPS,
                         "algorithmic_bytes": compress_bytes,
-                        "separate_launches": {"kernels": ["compress_k", "compress_v"], "us": t_app2 * 1e6,
-                                              "frac_hbm": compress_bytes / t_app2 / 1e9 / HBM_PEAK_GBPS}}
+                        "one_stream": {"us": t_app["one"] * 1e6,
+                                       "frac_hbm": compress_bytes / t_app["one"] / 1e9 / HBM_PEAK_GBPS},
+                        "separate_launches_one_stream": {
+                            "kernels": ["compress_k", "compress_v"], "us": t_app["separate"] * 1e6,
+                            "frac_hbm": compress_bytes / t_app["separate"] / 1e9 / HBM_PEAK_GBPS}}
     if pj_ev["fused"]:
         t_f = sum(a.elapsed_time(b) for a, b in pj_ev["fused"]) / len(pj_ev["fused"]) / 1e3
         t_u = sum(a.elapsed_time(b) for a, b in pj_ev["unfused"]) / len(pj_ev["unfused"]) / 1e3

@@ -210,3 +210,19 @@ def test_append_full_size_equals_one_shot():
     got, want = pk.pool_views(app, lay), pk.pool_views(one, lay)
     for key in want:
         assert torch.equal(got[key], want[key]), key
+    # the benchmark's schedule: one-launch appends, chunks alternating over two streams
+    # (512-token chunks touch disjoint 32-token groups, so they may run concurrently)
+    chunks = [(a, k[:, :, a:a + 512, :].contiguous(), v[:, :, a:a + 512, :].contiguous())
+              for a in range(0, cfg.n_tokens, 512)]
+    s1, s2 = torch.cuda.Stream(device=device()), torch.cuda.Stream(device=device())
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        two = new_pool(lay, fill=0x3C + rnd)
+        torch.cuda.synchronize()
+        for n, (a, kc, vc) in enumerate(chunks):
+            pk.polykv_append_kv(kc, vc, two, lay, a, stream=(s1, s2)[(n + rnd) % 2])
+        s1.synchronize()
+        s2.synchronize()
+        got = pk.pool_views(two, lay)
+        for key in want:
+            assert torch.equal(got[key], want[key]), (rnd, key)
