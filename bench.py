@@ -75,7 +75,7 @@ KERNELS = (
     ("attend_mfma", "k_attend_mfma<", ("attend_mfma.hip", "lds_dma.h", "polykv_internal.h")),
     ("attend_valu", "k_attend_valu<", ("attend.hip", "polykv_internal.h")),
     ("attend_tail", "k_attend_tail<", ("attend_tail.hip", "polykv_internal.h")),
-    ("compress_k", "k_compress_k", ("compress.hip", "codec.h", "polykv_internal.h")),
+    ("compress_k", "k_compress_k(", ("compress.hip", "codec.h", "polykv_internal.h")),
     ("compress_v", "k_compress_v_mfma<", ("compress.hip", "codec.h", "polykv_internal.h")),
     ("compress_kv", "k_compress_kv<", ("compress.hip", "codec.h", "polykv_internal.h")),
     ("compress_v_valu", "k_compress_v<", ("compress.hip", "codec.h", "polykv_internal.h")),
