@@ -351,8 +351,8 @@ def main():
             summarize_sq(args)
         return
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the pool would shard by KV head with no collective; see DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(the pool would shard by KV head, with no collective between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
