@@ -22,14 +22,20 @@ def _say(*a):
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
 def test_compress_full_config(cfg):
+    """Every workload at full size, compressed as the benchmark does (keys and values in
+    one launch, polykv_compress_kv) and checked against the oracle on every layer; the
+    two single-kind launches must give the same pool bytes."""
     _say("compress parity", cfg.name)
     lay = layout_for(cfg)
     k, v = upload_kv(cfg)
     pool = new_pool(lay)
-    pk.polykv_compress_k(k, pool, lay)
-    pk.polykv_compress_v(v, pool, lay)
+    pk.polykv_compress_kv(k, v, pool, lay)
+    sep = new_pool(lay)
+    pk.polykv_compress_k(k, sep, lay)
+    pk.polykv_compress_v(v, sep, lay)
     torch.cuda.synchronize()
-    del k, v
+    assert torch.equal(pool, sep)
+    del k, v, sep
     got = read_pool(pool, lay)
     H = cfg.n_kv_heads
     mism = coords = 0
