@@ -480,8 +480,7 @@ def main():
         px, pwk, pwv, kt, vt = proj
         for l in range(cfg.n_layers):
             pk.polykv_project_kv(px, pwk, pwv, kt, vt, cfg.n_kv_heads, cfg.head_dim, stream=stream)
-            pk.polykv_append_k(kt, pools[i % n_pools], lay, 0, layer_begin=l, layer_count=1, stream=stream)
-            pk.polykv_append_v(vt, pools[i % n_pools], lay, 0, layer_begin=l, layer_count=1, stream=stream)
+            pk.polykv_append_kv(kt, vt, pools[i % n_pools], lay, 0, layer_begin=l, layer_count=1, stream=stream)
 
     def dequant(i, which):
         # pool copy i -> fp16 K or V (into the compress inputs, which are not needed again)
@@ -606,7 +605,8 @@ def main():
         torch.cuda.synchronize()
 
         # Secondary figure: the K/V projection of every layer with the compression fused in,
-        # against the projection written as fp16 and then appended (the same pool bytes).
+        # against the projection written as fp16 and then appended by the one-launch key +
+        # value append (the same pool bytes), and against the library GEMM alone.
         # The pools end up holding the projected cache; nothing after this reads them.
         pj_ev = {"fused": [], "unfused": [], "library": []}
         if proj is not None:
