@@ -696,6 +696,7 @@ def main():
         "compress_GBps": compress_gbps, "compress_frac_hbm": compress_gbps / HBM_PEAK_GBPS,
         "compress_us": t_ckv * 1e6,
         "compress_kernel": "compress_kv (keys and values in one launch)",
+        "compress_traffic": _traffic("compress_kv", workload),
         "compress_separate": {
             "us": {"k": t_ck * 1e6, "v": t_cv * 1e6},
             "GBps": {"k": (fp16_bytes + cfg.kv_elems + cfg.kv_elems // 16) / t_ck / 1e9,
