@@ -536,19 +536,28 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
 
-        # Secondary figure: decode right after a 1 GiB write (cold caches and translations).
-        cold_us = []
+        # Secondary figures: single decode launches right after evicting the 256 MB Infinity
+        # Cache with 1 GiB of other traffic, outside the events: a 1 GiB read (the pool then
+        # comes from HBM), and a 1 GiB write (which also leaves that cache full of dirty
+        # lines that the decode's reads force back to HBM).
+        cold_us = {"read": [], "write": []}
         if not args.warm:
-            flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-            for s in range(4):
-                flush.add_(1)
+            flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+            flush32 = flush.view(torch.int32)
+            sink = torch.zeros(1, dtype=torch.int64, device=dev)
+            for s in range(8):
+                kind = "read" if s % 2 == 0 else "write"
+                if kind == "read":
+                    sink += flush32.sum(dtype=torch.int64)
+                else:
+                    flush.add_(1)
                 e0 = ev()
                 decode(0, s % D)
                 e1 = ev()
-                cold_us.append((e0, e1))
+                cold_us[kind].append((e0, e1))
             stream.synchronize()
-            cold_us = [a.elapsed_time(b) * 1e3 for a, b in cold_us]
-            del flush
+            cold_us = {k: [a.elapsed_time(b) * 1e3 for a, b in v] for k, v in cold_us.items()}
+            del flush, flush32, sink
 
         # Secondary figure: the private-tail merge after the pool decode (lse exported).
         tail_ev = []
@@ -705,8 +714,9 @@ def main():
             "GBps_both": compress_bytes / (t_ck + t_cv) / 1e9},
         "wall_ms_per_step": wall / args.steps * 1e3,
     }
-    if cold_us:
-        result["decode_us_after_1GiB_write"] = cold_us
+    if cold_us["read"]:
+        result["decode_us_after_1GiB_read"] = cold_us["read"]
+        result["decode_us_after_1GiB_write"] = cold_us["write"]
     if tail_ev:
         t_tail = sum(a.elapsed_time(b) for a, b in tail_ev) / len(tail_ev) / 1e3
         # fp16 tail K and V, q read, out read + written, lse read + written
