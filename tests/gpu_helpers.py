@@ -80,10 +80,11 @@ def pool_from_arrays(layout, k_codes, k_scales, v_planes, v_norms):
     return buf
 
 
-def check_v_codes(gpu_planes, want_planes, v_fp16, n_tokens):
+def check_v_codes(gpu_planes, want_planes, v_fp16, n_tokens, boundaries=None):
     """Apply the value-code rule to one set of tiles.
 
-    gpu_planes, want_planes: uint32 [tiles][G][3][d]; v_fp16: the input [tiles][T][d].
+    gpu_planes, want_planes: uint32 [tiles][G][3][d]; v_fp16: the input [tiles][T][d];
+    boundaries: the codebook's (default: the built-in one).
     Returns (number of mismatched coordinates, number of coordinates).
     """
     diff = np.bitwise_xor(gpu_planes, want_planes)
@@ -101,7 +102,7 @@ def check_v_codes(gpu_planes, want_planes, v_fp16, n_tokens):
                 bad.add((t, tok, i))
     bad = sorted(bad)
     # the oracle's fp64 rotated coordinates of the affected vectors
-    b = B32.astype(np.float64)
+    b = np.asarray(B32 if boundaries is None else boundaries, dtype=np.float64)
     for (t, tok, i) in bad:
         y = oracle.rotated_coordinates(v_fp16[t, tok])[i]
         assert np.min(np.abs(y - b)) < V_BOUNDARY_WINDOW, (t, tok, i, y)

@@ -41,10 +41,12 @@ def _pool(L, H, d, T, seed, k_scale=1.0, zero_v_tokens=()):
     return lay, torch.from_numpy(img).to(device()), op
 
 
-def check_v(got16, op, n_tokens):
-    """The value rule above; returns the number of elements that differ from the oracle."""
-    _, v64 = oracle.dequant_pool(op, C32, n_tokens)
-    _, want16 = oracle.dequant_fp16(op, C32, n_tokens)
+def check_v(got16, op, n_tokens, centroids=None):
+    """The value rule above; returns the number of elements that differ from the oracle.
+    centroids: the codebook's (default: the built-in one)."""
+    C = C32 if centroids is None else np.asarray(centroids, dtype=np.float32)
+    _, v64 = oracle.dequant_pool(op, C, n_tokens)
+    _, want16 = oracle.dequant_fp16(op, C, n_tokens)
     got16 = np.asarray(got16, dtype=np.float16).reshape(want16.shape)
     g = got16.astype(np.float64)
     w = want16.astype(np.float64)
@@ -53,7 +55,7 @@ def check_v(got16, op, n_tokens):
         return 0
     d = want16.shape[-1]
     codes = op["v_codes"] if "v_codes" in op else oracle.unpack_v_planes(op["v_planes"], n_tokens)
-    S = np.abs(np.asarray(C32, dtype=np.float64)[codes.astype(np.intp)]).sum(axis=-1, keepdims=True)
+    S = np.abs(np.asarray(C, dtype=np.float64)[codes.astype(np.intp)]).sum(axis=-1, keepdims=True)
     f = op["v_norms"].astype(np.float64)[..., None] / d
     E = (math.log2(d) * 2.0 ** -24 * S) * f + 2.0 ** -24 * np.abs(v64)
     E = np.broadcast_to(E, v64.shape)
