@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_attend_valu(AttendArgs a) {
     const PoolGeom& g = a.g;
     const int tid = threadIdx.x;
     const int H = g.n_kv_heads, T = g.n_tokens, G = a.gqa, A = a.n_agents;
-    const int R = A * G;
+    const int R = a.n_rows;  // rows of this launch; row r is row a.row_begin + r of the tile
     const int tile_local = blockIdx.x;
     const int l_local = tile_local / H, h = tile_local - l_local * H;
     const size_t tile = (size_t)(a.layer_begin + l_local) * H + h;
@@ -78,12 +78,12 @@ __global__ __launch_bounds__(256) void k_attend_valu(AttendArgs a) {
     const __half* vnorms = reinterpret_cast<const __half*>(a.pool + g.v_norms_off + tile * g.v_norms_stride);
     const size_t HG = (size_t)H * G;
 
-    // query rows r = agent * G + j  ->  q[l_local][agent][h * G + j][:]
+    // query rows: row_begin + r = agent * G + j  ->  q[l_local][agent][h * G + j][:]
     for (int idx = tid; idx < RP * D; idx += 256) {
         const int r = idx / D, i = idx - r * D;
         float val = 0.0f;
         if (r < R) {
-            const int ag = r / G, j = r - ag * G;
+            const int gr = a.row_begin + r, ag = gr / G, j = gr - ag * G;
             val = a.q[(((size_t)l_local * A + ag) * HG + (size_t)h * G + j) * D + i];
         }
         qT[i * QS + r] = val;
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void k_attend_valu(AttendArgs a) {
             }
         }
         const float inv = 1.0f / ((float)D * lrow[tid]);
-        const int ag = tid / G, j = tid - ag * G;
+        const int gr = a.row_begin + tid, ag = gr / G, j = gr - ag * G;
         // scores are in log2 units (scale * log2 e folded into q)
         if (a.lse)
             a.lse[((size_t)l_local * A + ag) * HG + (size_t)h * G + j] =
@@ -272,8 +272,7 @@ hipError_t launch_valu_t(const AttendArgs& a, hipStream_t s) {
 size_t attend_workspace_bytes(const PoolGeom&, int32_t, int32_t, int32_t, int32_t) { return 0; }
 
 hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s) {
-    const int rows = a.n_agents * a.gqa;
-    const bool small = rows <= 16;
+    const bool small = a.n_rows <= 16;
     switch (a.g.head_dim) {
         case 64: return small ? launch_valu_t<64, 4>(a, s) : launch_valu_t<64, 16>(a, s);
         case 128: return small ? launch_valu_t<128, 4>(a, s) : launch_valu_t<128, 16>(a, s);

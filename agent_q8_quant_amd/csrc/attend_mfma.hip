@@ -307,7 +307,7 @@ void k_attend_mfma(AttendArgs a) {
 
     const PoolGeom& g = a.g;
     const int H = g.n_kv_heads, T = g.n_tokens, G = a.gqa, A = a.n_agents;
-    const int R = A * G;
+    const int R = a.n_rows;  // rows of this launch; row r is row a.row_begin + r of the tile
     const int tile_local = blockIdx.x;
     const int l_local = tile_local / H, h = tile_local - l_local * H;
     const size_t tile = (size_t)(a.layer_begin + l_local) * H + h;
@@ -354,7 +354,7 @@ void k_attend_mfma(AttendArgs a) {
         for (int qb = 0; qb < QRB; ++qb) {
             const int r = 16 * (QSHARE ? stream : SRB * role + qb) + l16;
             if (r < R) {
-                const int ag = r / G, jj = r - ag * G;
+                const int gr = a.row_begin + r, ag = gr / G, jj = gr - ag * G;
                 const float* qrow = a.q + (((size_t)l_local * A + ag) * HG + (size_t)h * G + jj) * D;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
@@ -861,7 +861,7 @@ void k_attend_mfma(AttendArgs a) {
                 if (mv != -INFINITY) L += lw[v * ROWS + row] * __builtin_amdgcn_exp2f(mv - M);
             }
             const float inv = 1.0f / ((float)D * L * a.cb.fp16_scale);
-            const int ag = row / G, jj = row - ag * G;
+            const int gr = a.row_begin + row, ag = gr / G, jj = gr - ag * G;
             // scores are in log2 units and every p carries 2^-m
             if (a.lse && ft == 0)
                 a.lse[((size_t)l_local * A + ag) * HG + (size_t)h * G + jj] =
@@ -893,8 +893,7 @@ bool attend_mfma_supported(const PoolGeom& g, int32_t rows) {
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
-    const int rows = a.n_agents * a.gqa;
-    const int nrb = (rows + 15) / 16;
+    const int nrb = (a.n_rows + 15) / 16;
     if (a.g.head_dim == 128) {
         if (nrb == 1) return launch_t<128, 1, 1>(a, s);
         if (nrb == 2) return launch_t<128, 1, 2>(a, s);

@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -391,6 +393,12 @@ int polykv_dequant_v(const void* pool, const polykv_layout_t* layout, const poly
                                               (hipStream_t)hip_stream));
 }
 
+// Rows per tile are served in passes of at most POLYKV_ROWS_PER_PASS; every pass has at
+// least one row, so the kernel choice is the same for all of them.
+static int32_t first_pass_rows(int32_t n_agents, int32_t gqa) {
+    return (int32_t)std::min<int64_t>((int64_t)n_agents * gqa, POLYKV_ROWS_PER_PASS);
+}
+
 static int resolve_path(const polykv::PoolGeom& g, int32_t rows, int32_t path) {
     if (path == POLYKV_PATH_AUTO)
         return polykv::attend_mfma_supported(g, rows) ? POLYKV_PATH_MFMA : POLYKV_PATH_VALU;
@@ -402,19 +410,19 @@ int polykv_attend_path(const polykv_layout_t* layout, int32_t n_agents, int32_t 
     int rc = check_layout(layout);
     if (rc) return rc;
     if (n_agents < 1 || gqa < 1) return POLYKV_ERR_SHAPE;
-    if ((int64_t)n_agents * gqa > POLYKV_MAX_ROWS) return POLYKV_ERR_RANGE;
+    if ((int64_t)n_agents * gqa > INT32_MAX) return POLYKV_ERR_SHAPE;
     polykv::PoolGeom g = polykv::make_geom(*layout);
-    return resolve_path(g, n_agents * gqa, POLYKV_PATH_AUTO);
+    return resolve_path(g, first_pass_rows(n_agents, gqa), POLYKV_PATH_AUTO);
 }
 
 size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_agents,
                                      int32_t gqa, int32_t layer_count) {
     if (!layout || check_layout(layout) != POLYKV_OK || n_agents < 1 || gqa < 1 || layer_count < 1)
         return 0;
+    if ((int64_t)n_agents * gqa > INT32_MAX) return 0;
     polykv::PoolGeom g = polykv::make_geom(*layout);
-    int rows = n_agents * gqa;
     return polykv::attend_workspace_bytes(g, n_agents, gqa, layer_count,
-                                          resolve_path(g, rows, POLYKV_PATH_AUTO));
+                                          resolve_path(g, first_pass_rows(n_agents, gqa), POLYKV_PATH_AUTO));
 }
 
 static int attend_impl(const void* pool, const polykv_layout_t* layout,
@@ -429,7 +437,7 @@ static int attend_impl(const void* pool, const polykv_layout_t* layout,
     if (n_agents < 1 || gqa < 1) return POLYKV_ERR_SHAPE;
     if (!aligned(pool, 256) || !aligned(q, 16) || !aligned(out, 16)) return POLYKV_ERR_ALIGN;
     if ((rc = check_layers(*layout, layer_begin, layer_count))) return rc;
-    if ((int64_t)n_agents * gqa > POLYKV_MAX_ROWS) return POLYKV_ERR_RANGE;
+    if ((int64_t)n_agents * gqa > INT32_MAX) return POLYKV_ERR_SHAPE;
     if (!std::isfinite(softmax_scale)) return POLYKV_ERR_ARG;
     if (path < POLYKV_PATH_AUTO || path > POLYKV_PATH_MFMA) return POLYKV_ERR_ARG;
     const polykv_codebook_t& book = cb ? *cb : default_codebook();
@@ -438,9 +446,10 @@ static int attend_impl(const void* pool, const polykv_layout_t* layout,
     polykv::PoolGeom g = polykv::make_geom(*layout);
     g.n_tokens = n_valid;               // attend over tokens [0, n_valid) of every tile
     g.n_groups = (n_valid + 31) / 32;   // (strides and offsets stay those of the layout)
-    const int rows = n_agents * gqa;
-    path = resolve_path(g, rows, path);
-    if (path == POLYKV_PATH_MFMA && !polykv::attend_mfma_supported(g, rows)) return POLYKV_ERR_SHAPE;
+    const int32_t rows = n_agents * gqa;
+    path = resolve_path(g, first_pass_rows(n_agents, gqa), path);
+    if (path == POLYKV_PATH_MFMA && !polykv::attend_mfma_supported(g, first_pass_rows(n_agents, gqa)))
+        return POLYKV_ERR_SHAPE;
     size_t need = polykv::attend_workspace_bytes(g, n_agents, gqa, layer_count, path);
     if (need > 0 && (!workspace || workspace_bytes < need)) return POLYKV_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 16)) return POLYKV_ERR_ALIGN;
@@ -460,8 +469,15 @@ static int attend_impl(const void* pool, const polykv_layout_t* layout,
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     hipStream_t s = (hipStream_t)hip_stream;
-    return launch_rc(path == POLYKV_PATH_MFMA ? polykv::launch_attend_mfma(a, s)
-                                              : polykv::launch_attend_valu(a, s));
+    // one launch per pass of at most POLYKV_ROWS_PER_PASS rows; each streams the pool once
+    for (int64_t r0 = 0; r0 < rows; r0 += POLYKV_ROWS_PER_PASS) {
+        a.row_begin = (int32_t)r0;
+        a.n_rows = (int32_t)std::min<int64_t>(POLYKV_ROWS_PER_PASS, rows - r0);
+        rc = launch_rc(path == POLYKV_PATH_MFMA ? polykv::launch_attend_mfma(a, s)
+                                                : polykv::launch_attend_valu(a, s));
+        if (rc) return rc;
+    }
+    return POLYKV_OK;
 }
 
 int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
@@ -503,8 +519,9 @@ int polykv_attend_tail_merge(const polykv_layout_t* layout, const float* q, floa
     int rc = check_layout(layout);
     if (rc) return rc;
     if (n_agents < 1 || gqa < 1 || tail_cap < 0) return POLYKV_ERR_SHAPE;
-    if ((int64_t)n_agents * gqa > POLYKV_MAX_ROWS) return POLYKV_ERR_RANGE;
     if (layer_count < 1 || layer_count > layout->shape.n_layers) return POLYKV_ERR_RANGE;
+    // one workgroup per (layer, agent, KV head)
+    if ((int64_t)layer_count * n_agents * layout->shape.n_kv_heads > INT32_MAX) return POLYKV_ERR_SHAPE;
     if (!std::isfinite(softmax_scale)) return POLYKV_ERR_ARG;
     if (tail_cap > 0 && (!tail_k || !tail_v)) return POLYKV_ERR_NULL;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4) || !aligned(tail_len, 4))

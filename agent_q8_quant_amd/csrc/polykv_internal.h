@@ -94,6 +94,9 @@ struct AttendArgs {
     float* out;
     float* lse;  // optional [layer_count][n_agents][H * gqa]: ln sum_t exp(scale q . k_t)
     int32_t n_agents, gqa, layer_begin, layer_count;
+    // the launch serves rows row_begin .. row_begin + n_rows - 1 of every tile, row r being
+    // agent r / gqa, query head h * gqa + r % gqa (1 <= n_rows <= 64)
+    int32_t row_begin, n_rows;
     float softmax_scale;
     void* workspace;
     size_t workspace_bytes;

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libpolykv.so")
 
 POLYKV_OK = 0
 POLYKV_PATH_AUTO, POLYKV_PATH_VALU, POLYKV_PATH_MFMA = 0, 1, 2
-POLYKV_MAX_ROWS = 64
+POLYKV_ROWS_PER_PASS = 64  # query rows one decode launch serves per pool tile
 
 EXPORTED_SYMBOLS = (
     "polykv_pool_layout", "polykv_codebook_default", "polykv_compress_k", "polykv_compress_v",

@@ -44,8 +44,7 @@ extern "C" {
 #define POLYKV_ERR_SHAPE (-2)      /* head_dim not in {64,128,256}, a count < 1, or       */
                                    /* a size that overflows                               */
 #define POLYKV_ERR_ALIGN (-3)      /* pool not 256-B aligned, another buffer not 16-B     */
-#define POLYKV_ERR_RANGE (-4)      /* layer range outside the pool, or rows per tile      */
-                                   /* (n_agents * gqa) above POLYKV_MAX_ROWS              */
+#define POLYKV_ERR_RANGE (-4)      /* layer or token range outside the pool               */
 #define POLYKV_ERR_WORKSPACE (-5)  /* workspace smaller than polykv_attend_workspace_bytes */
 #define POLYKV_ERR_DEVICE (-6)     /* no HIP device, or the current device is not gfx950  */
 #define POLYKV_ERR_LAUNCH (-7)     /* a kernel launch failed (hipGetLastError)             */
@@ -53,7 +52,9 @@ extern "C" {
 #define POLYKV_ERR_LAYOUT (-9)     /* layout struct does not match polykv_pool_layout     */
 #define POLYKV_ERR_ARG (-10)       /* another argument out of its domain                  */
 
-#define POLYKV_MAX_ROWS 64         /* agents x query heads per KV head, per pool tile     */
+#define POLYKV_ROWS_PER_PASS 64    /* query rows (agents x query heads of a KV head) one  */
+                                   /* decode launch serves per pool tile; more rows take */
+                                   /* further launches, each reading the pool once       */
 
 /* Kernel choice for polykv_compress_v_path and polykv_attend_shared_path. */
 #define POLYKV_PATH_AUTO 0   /* matrix cores where supported (head_dim 64/128), else VALU */
@@ -260,7 +261,7 @@ int polykv_dequant_v(const void* pool, const polykv_layout_t* layout, const poly
 
 
 /* The decode kernel POLYKV_PATH_AUTO selects for these arguments (POLYKV_PATH_VALU or
- * POLYKV_PATH_MFMA), or a negative error code (NULL, SHAPE, RANGE, LAYOUT). Host only. */
+ * POLYKV_PATH_MFMA), or a negative error code (NULL, SHAPE, LAYOUT). Host only. */
 int polykv_attend_path(const polykv_layout_t* layout, int32_t n_agents, int32_t gqa);
 
 /* Device bytes of workspace polykv_attend_shared needs for these arguments (0 if none). */
@@ -278,6 +279,10 @@ size_t polykv_attend_workspace_bytes(const polykv_layout_t* layout, int32_t n_ag
  *  cb: host codebook or NULL for the default; only the centroids are used.
  *  workspace: device, at least polykv_attend_workspace_bytes(...) bytes (may be NULL
  *       when that is 0).
+ *  n_agents * gqa may be any count up to INT32_MAX (SHAPE above that): the rows of a tile
+ *  are served in passes of POLYKV_ROWS_PER_PASS rows in agent-major order, one launch per
+ *  pass, so each pass reads the whole pool once. Arguments are checked before the first
+ *  launch.
  * Errors: NULL, SHAPE, ALIGN, RANGE, LAYOUT, CODEBOOK, WORKSPACE, DEVICE, LAUNCH.
  */
 int polykv_attend_shared(const void* pool, const polykv_layout_t* layout,

@@ -133,10 +133,42 @@ static void decode() {
     float* out = static_cast<float*>(P(0x400000));
     float* lse = static_cast<float*>(P(0x500000));
     CHECK(polykv_attend_path(&l, 15, 4) == POLYKV_PATH_MFMA);
-    CHECK(polykv_attend_path(&l, 17, 4) < 0);   // 68 rows per tile
+    CHECK(polykv_attend_path(&l, 17, 4) == POLYKV_PATH_MFMA);   // 68 rows: two passes
+    CHECK(polykv_attend_path(&l, 1 << 20, 1 << 12) == POLYKV_ERR_SHAPE);
     CHECK(polykv_attend_workspace_bytes(&l, 15, 4, 2) == 0);
+    g_stub.n_passes = 0;
     CHECK(polykv_attend_shared(pool, &l, nullptr, q, out, 15, 4, 0.088f, 0, 2, nullptr, 0, nullptr) == POLYKV_OK);
     CHECK(std::strcmp(g_stub.last, "attend_mfma") == 0 && g_stub.a0 == 15 && g_stub.a1 == 4);
+    CHECK(g_stub.n_passes == 1 && g_stub.row_begin[0] == 0 && g_stub.n_rows[0] == 60);
+    // rows beyond one pass: consecutive ranges of at most POLYKV_ROWS_PER_PASS rows, every
+    // launch with the full agent count (the strides of q, out and lse)
+    struct RowCase { int agents, gqa; int passes; int last; };
+    for (const RowCase& rc : {RowCase{16, 4, 1, 64}, RowCase{17, 4, 2, 4}, RowCase{33, 4, 3, 4},
+                              RowCase{1, 130, 3, 2}, RowCase{200, 1, 4, 8}}) {
+        for (int path : {POLYKV_PATH_AUTO, POLYKV_PATH_VALU, POLYKV_PATH_MFMA}) {
+            g_stub.n_passes = 0;
+            CHECK(polykv_attend_shared_path(pool, &l, nullptr, q, out, rc.agents, rc.gqa, 0.088f, 0, 2, nullptr, 0,
+                                            nullptr, path) == POLYKV_OK);
+            CHECK(g_stub.n_passes == rc.passes);
+            CHECK(g_stub.a0 == rc.agents && g_stub.a1 == rc.gqa);
+            for (int i = 0; i < g_stub.n_passes && i < 16; ++i) {
+                CHECK(g_stub.row_begin[i] == POLYKV_ROWS_PER_PASS * i);
+                CHECK(g_stub.n_rows[i] == (i + 1 < rc.passes ? POLYKV_ROWS_PER_PASS : rc.last));
+            }
+        }
+    }
+    // a failing launch stops the passes and is reported
+    g_stub.n_passes = 0;
+    g_stub.launch_status = hipErrorLaunchFailure;
+    CHECK(polykv_attend_shared(pool, &l, nullptr, q, out, 33, 4, 0.088f, 0, 2, nullptr, 0, nullptr) ==
+          POLYKV_ERR_LAUNCH);
+    CHECK(g_stub.n_passes == 1);
+    g_stub.launch_status = hipSuccess;
+    // an argument error is found before the first pass
+    g_stub.n_passes = 0;
+    CHECK(polykv_attend_shared_path(pool, &l, nullptr, q, out, 33, 4, 0.088f, 0, 2, nullptr, 0, nullptr, 7) ==
+          POLYKV_ERR_ARG);
+    CHECK(g_stub.n_passes == 0);
     CHECK(polykv_attend_shared_path(pool, &l, nullptr, q, out, 15, 4, 0.088f, 0, 2, nullptr, 0, nullptr,
                                     POLYKV_PATH_VALU) == POLYKV_OK);
     CHECK(std::strcmp(g_stub.last, "attend_valu") == 0);

@@ -82,10 +82,19 @@ hipError_t launch_dequant_v(const uint8_t*, void*, const PoolGeom& g, const Code
     return record("dequant_v", &g, lb, lc);
 }
 size_t attend_workspace_bytes(const PoolGeom&, int32_t, int32_t, int32_t, int32_t) { return 0; }
+static void record_pass(const AttendArgs& a) {
+    if (g_stub.n_passes < 16) {
+        g_stub.row_begin[g_stub.n_passes] = a.row_begin;
+        g_stub.n_rows[g_stub.n_passes] = a.n_rows;
+    }
+    g_stub.n_passes++;
+}
 hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t) {
+    record_pass(a);
     return record("attend_valu", &a.g, a.n_agents, a.gqa);
 }
 hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t) {
+    record_pass(a);
     return record("attend_mfma", &a.g, a.n_agents, a.gqa);
 }
 bool attend_mfma_supported(const PoolGeom& g, int32_t rows) {

@@ -15,6 +15,9 @@ struct StubState {
     polykv::CodebookHalf cb = {};
     int32_t a0 = 0, a1 = 0;
     bool valu = false;
+    // row ranges of the decode launches since the driver last cleared n_passes
+    int n_passes = 0;
+    int32_t row_begin[16] = {0}, n_rows[16] = {0};
 };
 
 extern StubState g_stub;

@@ -129,7 +129,9 @@ def test_attend_validation(L):
     assert _attend(L, lay, n_agents=0) == -2
     assert _attend(L, lay, q=ctypes.c_void_p(0x10004)) == -3
     assert _attend(L, lay, lb=2, lc=1) == -4
-    assert _attend(L, lay, n_agents=17, gqa=4) == -4    # 68 rows > 64
+    # any row count: 68 rows pass every check (two launches); only the device is missing here
+    assert _attend(L, lay, n_agents=17, gqa=4) == -6
+    assert _attend(L, lay, n_agents=1 << 20, gqa=1 << 12) == -2   # rows overflow int32
     assert _attend(L, lay, scale=float("inf")) == -10
     assert _attend(L, lay, path=3) == -10
     cb = pk.polykv_codebook_default()
@@ -151,7 +153,10 @@ def test_attend_path_choice(L):
     lay = _layout()
     assert L.polykv_attend_path(None, 1, 1) == -1
     assert L.polykv_attend_path(ctypes.byref(lay), 0, 1) == -2
-    assert L.polykv_attend_path(ctypes.byref(lay), 17, 4) == -4
+    # more rows than one launch serves: the same kernel for every pass
+    assert L.polykv_attend_path(ctypes.byref(lay), 17, 4) == pk.POLYKV_PATH_MFMA
+    assert pk.polykv_attend_path(pk.polykv_pool_layout(2, 2, 256, 100), 200, 1) == pk.POLYKV_PATH_VALU
+    assert L.polykv_attend_path(ctypes.byref(lay), 1 << 20, 1 << 12) == -2
     bad = pk.polykv_pool_layout(2, 2, 128, 100)
     bad.k_codes_off += 16
     assert L.polykv_attend_path(ctypes.byref(bad), 1, 1) == -9
@@ -173,7 +178,8 @@ def test_tail_merge_validation(L):
     assert call(tk=None) == -1          # a non-empty tail needs its buffers
     assert call(A=0) == -2
     assert call(cap=-1) == -2
-    assert call(A=17, G=4) == -4
+    assert call(A=17, G=4) == -6        # any row count; no device here
+    assert call(A=1 << 30) == -2        # layers x agents x heads workgroups overflow int32
     assert call(lc=3) == -4             # more layers than the layout holds
     assert call(scale=float("nan")) == -10
     assert call(q=vp(0x100004)) == -3
