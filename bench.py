@@ -659,6 +659,17 @@ def main():
                     cp_ev.append((e0, e1))
         stream.synchronize()
         del cp_dst
+        # and a plain read: a library reduction over one pool copy (as int64 words), the
+        # source rotating the same way
+        rd_ev = []
+        with torch.cuda.stream(stream):
+            for i in range(n_pools + 12):
+                e0 = ev()
+                pools[i % n_pools].view(torch.int64).sum()
+                e1 = ev()
+                if i >= n_pools:
+                    rd_ev.append((e0, e1))
+        stream.synchronize()
 
     step_ms = [r[0].elapsed_time(r[-1]) for r in rec]
     ckv_ms = [r[0].elapsed_time(r[1]) for r in rec]
@@ -773,6 +784,11 @@ def main():
         "what": "torch copy of one pool copy (read + write), sources rotating like the decode",
         "bytes": 2 * lay.total_bytes, "us": t_cp * 1e6, "GBps": 2 * lay.total_bytes / t_cp / 1e9,
         "frac_hbm": 2 * lay.total_bytes / t_cp / 1e9 / HBM_PEAK_GBPS}
+    t_rd = sum(a.elapsed_time(b) for a, b in rd_ev) / len(rd_ev) / 1e3
+    result["device_read_reference"] = {
+        "what": "torch int64 sum over one pool copy (read only), sources rotating like the decode",
+        "bytes": lay.total_bytes, "us": t_rd * 1e6, "GBps": lay.total_bytes / t_rd / 1e9,
+        "frac_hbm": lay.total_bytes / t_rd / 1e9 / HBM_PEAK_GBPS}
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         n = args.cpu_sample_layers or cfg.n_layers
