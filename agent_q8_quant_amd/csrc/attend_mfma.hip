@@ -413,6 +413,14 @@ void k_attend_mfma(AttendArgs a) {
                 h8 hi, lo;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) hi[e] = (_Float16)x[e];
+                // lo must be formed from the hi that is stored. Left to itself the compiler
+                // recomputes hi for this subtraction from the unrounded product q * qs (a
+                // mixed-precision fma), which rounds differently from the stored hi whenever
+                // the fp32 x falls on an fp16 tie; hi + lo then misses x by one fp16 ulp.
+                // The empty asm makes the stored hi opaque, so it is the one used.
+                uint4 hu = __builtin_bit_cast(uint4, hi);
+                asm volatile("" : "+v"(hu.x), "+v"(hu.y), "+v"(hu.z), "+v"(hu.w));
+                hi = __builtin_bit_cast(h8, hu);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) lo[e] = (_Float16)(x[e] - (float)hi[e]);
                 if constexpr (QSHARE) {
@@ -513,16 +521,20 @@ void k_attend_mfma(AttendArgs a) {
                         S[tb][rb] = f4{init, init, init, init};
                     }
                     // two-stage pipeline over the q8 blocks: block b+1's conversion and its
-                    // hi products are issued before block b's scale FMAs read its results
+                    // lo products are issued before block b's scale FMAs read its results.
+                    // The lo products are summed first, into a zero accumulator, and the hi
+                    // products then added to that sum: added the other way round, into a sum
+                    // already holding the large hi products, their low bits are cut off (a
+                    // bias common to all tokens of a row, visible in the exported lse)
                     const uint8_t* kt = st + 16 * D * tb;
                     h8 ak = codes_to_h8(*reinterpret_cast<const uint2*>(kt + kfrag[0]));
                     f4 acc[SRB];
 #pragma unroll
                     for (int rb = 0; rb < SRB; ++rb)
-                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qh[rb][0], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, ql[rb][0], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
                     for (int rb = 0; rb < SRB; ++rb)
-                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, ql[rb][0], acc[rb], 0, 0, 0);
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qh[rb][0], acc[rb], 0, 0, 0);
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         f4 accn[SRB];
@@ -531,7 +543,7 @@ void k_attend_mfma(AttendArgs a) {
                             akn = codes_to_h8(*reinterpret_cast<const uint2*>(kt + kfrag[b + 1]));
 #pragma unroll
                             for (int rb = 0; rb < SRB; ++rb)
-                                accn[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, qh[rb][b + 1], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                                accn[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, ql[rb][b + 1], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
                         }
 #pragma unroll
                         for (int rb = 0; rb < SRB; ++rb)
@@ -543,7 +555,7 @@ void k_attend_mfma(AttendArgs a) {
                         if (b + 1 < NB) {
 #pragma unroll
                             for (int rb = 0; rb < SRB; ++rb)
-                                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, ql[rb][b + 1], accn[rb], 0, 0, 0);
+                                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, qh[rb][b + 1], accn[rb], 0, 0, 0);
                             ak = akn;
                         }
                     }
