@@ -521,20 +521,16 @@ void k_attend_mfma(AttendArgs a) {
                         S[tb][rb] = f4{init, init, init, init};
                     }
                     // two-stage pipeline over the q8 blocks: block b+1's conversion and its
-                    // lo products are issued before block b's scale FMAs read its results.
-                    // The lo products are summed first, into a zero accumulator, and the hi
-                    // products then added to that sum: added the other way round, into a sum
-                    // already holding the large hi products, their low bits are cut off (a
-                    // bias common to all tokens of a row, visible in the exported lse)
+                    // hi products are issued before block b's scale FMAs read its results
                     const uint8_t* kt = st + 16 * D * tb;
                     h8 ak = codes_to_h8(*reinterpret_cast<const uint2*>(kt + kfrag[0]));
                     f4 acc[SRB];
 #pragma unroll
                     for (int rb = 0; rb < SRB; ++rb)
-                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, ql[rb][0], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qh[rb][0], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
                     for (int rb = 0; rb < SRB; ++rb)
-                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, qh[rb][0], acc[rb], 0, 0, 0);
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, ql[rb][0], acc[rb], 0, 0, 0);
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         f4 accn[SRB];
@@ -543,7 +539,7 @@ void k_attend_mfma(AttendArgs a) {
                             akn = codes_to_h8(*reinterpret_cast<const uint2*>(kt + kfrag[b + 1]));
 #pragma unroll
                             for (int rb = 0; rb < SRB; ++rb)
-                                accn[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, ql[rb][b + 1], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                                accn[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, qh[rb][b + 1], f4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
                         }
 #pragma unroll
                         for (int rb = 0; rb < SRB; ++rb)
@@ -555,7 +551,7 @@ void k_attend_mfma(AttendArgs a) {
                         if (b + 1 < NB) {
 #pragma unroll
                             for (int rb = 0; rb < SRB; ++rb)
-                                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, qh[rb][b + 1], accn[rb], 0, 0, 0);
+                                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(akn, ql[rb][b + 1], accn[rb], 0, 0, 0);
                             ak = akn;
                         }
                     }
