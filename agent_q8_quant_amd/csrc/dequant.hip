@@ -55,67 +55,57 @@ __global__ __launch_bounds__(256) void k_dequant_k(const uint8_t* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------------------
-// Values. An item is one 32-token group of a tile for head_dim 128 and 256 (lane l holds
-// token l % 32, coordinates (l / 32) * d/2 .. + d/2 - 1) and two consecutive groups for
-// head_dim 64 (lane l holds token l % 32 of group l / 32, all 64 coordinates). Each wave
-// walks items with a grid stride and keeps the next item's plane words and norm in
-// registers while it works on the current one. Per item:
+// Values. An item is one 32-token group of a tile; each wave walks items with a grid stride
+// and keeps the next item's plane words and norms in registers while it works on the
+// current one. Every lane holds 32 coordinates of one token: LPT = d/32 lanes per token,
+// lane l = t + TPP q (TPP = 64/LPT tokens per pass) holds token t of the pass and
+// coordinates 32 q .. 32 q + 31, and the wave covers its group in 32/TPP passes. Per item:
 // 1. the plane words (3 x d per group, as stored) go from registers to the wave's LDS area;
-// 2. lane l reads, per coordinate, the three words of its half and takes bit l % 32 of
-//    each: the code, whose centroid comes from an 8-entry LDS table;
-// 3. the FWHT runs in registers over the lane's coordinates, and for d >= 128 one last
-//    butterfly pairs lane l with lane l ^ 32 (the other coordinate half), one register
-//    swap per two coordinates;
+// 2. per coordinate, the lane takes bit t of its three words: the code, whose centroid
+//    comes from an 8-entry LDS table;
+// 3. the FWHT runs in registers up to distance 16, then across lanes: for d = 256 first
+//    distance 32 between lanes l and l ^ 8 (a DPP row rotation), then, for the two highest
+//    bits of q, distances 32 (d = 128) or 64 (d = 256) between l and l ^ 16 and d/2 between
+//    l and l ^ 32 (d = 64: only the last), one register swap and two additions per
+//    coordinate pair each. A swap of registers e and e + 16 hands the lane with the lower
+//    bit both values of its local coordinate e and the other lane both values of e + 16, so
+//    each swap stage halves the run a lane holds; a lane ends with two runs of 16 coordinates,
+//    c0 .. c0 + 15 and d/2 + c0 .. + 15;
 // 4. times n / d, rounded to fp16, stored as 16-byte pieces.
+// Keeping 32 coordinates per lane (not d/2) halves the registers of d = 128 and so doubles
+// the waves a SIMD holds, which hides the latency of the lookup and shuffle chains.
 // ---------------------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
-    static constexpr int HALVES = D == 64 ? 1 : 2;   // lanes per token
-    static constexpr int CPL = D / HALVES;           // coordinates per lane
-    static constexpr int GPW = D == 64 ? 2 : 1;      // groups per item
-    static constexpr int WORDS = GPW * 3 * D;        // plane words per item
-    static constexpr int PIECES = WORDS / 4;         // 16-byte pieces per item
+    static constexpr int LPT = D / 32;               // lanes per token
+    static constexpr int TPP = 64 / LPT;             // tokens per pass
+    static constexpr int PASSES = 32 / TPP;
+    static constexpr int WORDS = 3 * D;              // plane words per group
+    static constexpr int PIECES = WORDS / 4;         // 16-byte pieces per group
     static constexpr int PPL = (PIECES + 63) / 64;   // pieces per lane
 };
 
-// Where item `item` lives, and its plane words and this lane's norm fetched into registers.
+// first coordinate of the lane's lower run after the cross-lane stages (q: the lane's
+// 32-coordinate slot before them)
 template <int D>
-struct DqItem {
-    uint32_t tile_local;
-    int g0, n_grp, token;
-    bool valid;
-};
-
-template <int D>
-__device__ __forceinline__ DqItem<D> dq_item(uint32_t item, uint32_t items_per_tile, const PoolGeom& g, int lane) {
-    using C = DqCfg<D>;
-    DqItem<D> it;
-    it.tile_local = item / items_per_tile;
-    const uint32_t gi = item - it.tile_local * items_per_tile;
-    it.g0 = (int)gi * C::GPW;
-    it.n_grp = min(C::GPW, g.n_groups - it.g0);
-    const int half = lane >> 5, t = lane & 31;
-    it.token = 32 * (C::GPW == 2 ? it.g0 + half : it.g0) + t;
-    it.valid = it.token < g.n_tokens && (C::GPW == 1 || half < it.n_grp);
-    return it;
+__device__ __forceinline__ int dq_run_start(int q) {
+    if constexpr (D == 64) return 16 * q;
+    else if constexpr (D == 128) return 16 * (q & 1) + 32 * (q >> 1);
+    else return 32 * (q & 1) + 16 * ((q >> 1) & 1) + 64 * (q >> 2);
 }
 
-template <int D>
-__device__ __forceinline__ void dq_fetch(const DqItem<D>& it, const uint8_t* pool, const PoolGeom& g,
-                                         int32_t layer_begin, int lane, u4 (&pf)[DqCfg<D>::PPL],
-                                         uint32_t& norm_bits) {
-    using C = DqCfg<D>;
-    const size_t tile = (size_t)layer_begin * g.n_kv_heads + it.tile_local;
-    const u4* src = reinterpret_cast<const u4*>(pool + g.v_planes_off + tile * g.v_planes_stride +
-                                                (size_t)it.g0 * (3 * D * 4));
-    const int n_pieces = it.n_grp * 3 * D / 4;
+// one cross-lane butterfly stage by register swaps (see above)
+template <bool ROW16>
+__device__ __forceinline__ void dq_swap_stage(float (&x)[32]) {
 #pragma unroll
-    for (int i = 0; i < C::PPL; ++i) {
-        const int piece = lane + 64 * i;
-        if (piece < n_pieces) pf[i] = src[piece];
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t a0 = __float_as_uint(x[e]), b0 = __float_as_uint(x[e + 16]);
+        const auto sw = ROW16 ? __builtin_amdgcn_permlane16_swap(a0, b0, false, false)
+                              : __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const float a = __uint_as_float(sw[0]), b = __uint_as_float(sw[1]);
+        x[e] = a + b;
+        x[e + 16] = a - b;
     }
-    const uint16_t* norms = reinterpret_cast<const uint16_t*>(pool + g.v_norms_off + tile * g.v_norms_stride);
-    norm_bits = it.valid ? norms[it.token] : 0u;
 }
 
 template <int D>
@@ -124,7 +114,7 @@ __global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ p
                                                    uint32_t items_per_tile, uint32_t n_items,
                                                    __half* __restrict__ out) {
     using C = DqCfg<D>;
-    constexpr int CPL = C::CPL;
+    constexpr int TPP = C::TPP, PASSES = C::PASSES;
     __shared__ __attribute__((aligned(16))) uint32_t words[4][C::WORDS];
     __shared__ float ctab[8];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -140,97 +130,112 @@ __global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ p
     uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4u + (uint32_t)w));
     if (item >= n_items) return;
     const int T = g.n_tokens;
-    const int half = lane >> 5, t = lane & 31;
-    const int coord0 = C::GPW == 2 ? 0 : half * CPL;
-    const uint32_t* wb = &words[w][(C::GPW == 2 ? half * 3 * D : 0) + coord0];
+    const int tl = lane % TPP, q = lane / TPP;
+    const uint32_t* wb = &words[w][32 * q];
     u4* stage = reinterpret_cast<u4*>(&words[w][0]);
+    const int run0 = dq_run_start<D>(q);
 
+    // the item's plane words and this lane's norms (one per pass), fetched one item ahead
     u4 pf[C::PPL];
-    uint32_t norm_bits;
-    DqItem<D> it = dq_item<D>(item, items_per_tile, g, lane);
-    dq_fetch<D>(it, pool, g, layer_begin, lane, pf, norm_bits);
+    uint32_t nb[PASSES];
+    uint32_t tile_next = 0;
+    int g_next = 0;
+    auto fetch = [&](uint32_t it) {
+        tile_next = it / items_per_tile;
+        g_next = (int)(it - tile_next * items_per_tile);
+        const size_t tile = (size_t)layer_begin * g.n_kv_heads + tile_next;
+        const u4* src = reinterpret_cast<const u4*>(pool + g.v_planes_off + tile * g.v_planes_stride +
+                                                    (size_t)g_next * (3 * D * 4));
+#pragma unroll
+        for (int i = 0; i < C::PPL; ++i) {
+            const int piece = lane + 64 * i;
+            if (piece < C::PIECES) pf[i] = src[piece];
+        }
+        const uint16_t* nrm = reinterpret_cast<const uint16_t*>(pool + g.v_norms_off + tile * g.v_norms_stride);
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int tok = 32 * g_next + TPP * p + tl;
+            nb[p] = tok < T ? nrm[tok] : 0u;
+        }
+    };
+    fetch(item);
     while (true) {
         // 1. this item's words into LDS (the previous item's reads are complete: their
         //    results were consumed before its stores)
-        {
-            const int n_pieces = it.n_grp * 3 * D / 4;
 #pragma unroll
-            for (int i = 0; i < C::PPL; ++i) {
-                const int piece = lane + 64 * i;
-                if (piece < n_pieces) stage[piece] = pf[i];
-            }
+        for (int i = 0; i < C::PPL; ++i) {
+            const int piece = lane + 64 * i;
+            if (piece < C::PIECES) stage[piece] = pf[i];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const DqItem<D> cur = it;
-        const float f = __half2float(__ushort_as_half((unsigned short)norm_bits)) * (1.0f / (float)D);
+        const uint32_t tile_local = tile_next;
+        const int g0 = g_next;
+        uint32_t ncur[PASSES];
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) ncur[p] = nb[p];
         const uint32_t next = item + stride;
-        if (next < n_items) {
-            it = dq_item<D>(next, items_per_tile, g, lane);
-            dq_fetch<D>(it, pool, g, layer_begin, lane, pf, norm_bits);  // in flight meanwhile
-        }
-
-        // 2. codes -> centroids
-        float x[CPL];
+        if (next < n_items) fetch(next);  // in flight meanwhile
 #pragma unroll
-        for (int c = 0; c < CPL; c += 4) {
-            const u4 p0 = *reinterpret_cast<const u4*>(wb + c);
-            const u4 p1 = *reinterpret_cast<const u4*>(wb + D + c);
-            const u4 p2 = *reinterpret_cast<const u4*>(wb + 2 * D + c);
+        for (int pass = 0; pass < PASSES; ++pass) {
+            const int t = TPP * pass + tl;  // token within the group
+            const int token = 32 * g0 + t;
+            const float f = __half2float(__ushort_as_half((unsigned short)ncur[pass])) * (1.0f / (float)D);
+            // 2. codes -> centroids
+            float x[32];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t code = __builtin_amdgcn_ubfe(p0[e], t, 1) | (__builtin_amdgcn_ubfe(p1[e], t, 1) << 1) |
-                                      (__builtin_amdgcn_ubfe(p2[e], t, 1) << 2);
-                x[c + e] = ctab[code];
-            }
-        }
-        // 3. Sylvester FWHT over the lane's coordinates (pairs at distance h become (a+b, a-b))
+            for (int c = 0; c < 32; c += 4) {
+                const u4 p0 = *reinterpret_cast<const u4*>(wb + c);
+                const u4 p1 = *reinterpret_cast<const u4*>(wb + D + c);
+                const u4 p2 = *reinterpret_cast<const u4*>(wb + 2 * D + c);
 #pragma unroll
-        for (int h = 1; h < CPL; h <<= 1)
-#pragma unroll
-            for (int e = 0; e < CPL; ++e)
-                if (!(e & h)) {
-                    const float a = x[e], b = x[e + h];
-                    x[e] = a + b;
-                    x[e + h] = a - b;
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t code = __builtin_amdgcn_ubfe(p0[e], t, 1) | (__builtin_amdgcn_ubfe(p1[e], t, 1) << 1) |
+                                          (__builtin_amdgcn_ubfe(p2[e], t, 1) << 2);
+                    x[c + e] = ctab[code];
                 }
-        // 4. scale by n / d and store 16-byte pieces of `n` consecutive coordinates
-        auto store = [&](const float* v, int first, int n) {
-            u4* o = reinterpret_cast<u4*>(out + ((size_t)cur.tile_local * T + cur.token) * D + first);
-#pragma unroll
-            for (int c = 0; c < n; c += 8) {
-                uint32_t q[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    q[e] = (uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e] * f)) |
-                           ((uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e + 1] * f)) << 16);
-                o[c / 8] = u4{q[0], q[1], q[2], q[3]};
             }
-        };
-        if constexpr (C::HALVES == 2) {
-            // the last butterfly pairs coordinate i (lane l, lower half) with i + d/2 (lane
-            // l ^ 32). One swap of registers e and e + HP (HP = d/4) hands the lower lane both
-            // values of coordinate e and the upper lane both values of coordinate e + HP:
-            // sw[0] is the lower half's value and sw[1] the upper half's in either lane. So
-            // lane l finishes coordinates base + e and base + e + d/2 (e < HP), base = HP for
-            // the upper lane: one swap and two additions per pair.
-            constexpr int HP = CPL / 2;
-            float lo[HP], hi[HP];
+            // 3. Sylvester FWHT: pairs at distance h become (a + b, a - b)
 #pragma unroll
-            for (int e = 0; e < HP; ++e) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[e]), __float_as_uint(x[e + HP]), false, false);
-                const float a = __uint_as_float(sw[0]), b = __uint_as_float(sw[1]);
-                lo[e] = a + b;
-                hi[e] = a - b;
+            for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+                for (int e = 0; e < 32; ++e)
+                    if (!(e & h)) {
+                        const float a = x[e], b = x[e + h];
+                        x[e] = a + b;
+                        x[e + h] = a - b;
+                    }
+            if constexpr (D == 256) {
+                // distance 32 between lanes l and l ^ 8 (rotation by 8 within a row of 16):
+                // the lane with bit 3 clear keeps a + b, the other b' - a' of its own pair
+                const float sg = (q & 1) ? -1.0f : 1.0f;
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(x[e]), 0x128, 0xF, 0xF, false);
+                    x[e] = __builtin_fmaf(sg, x[e], __int_as_float(o));
+                }
             }
-            if (cur.valid) {
-                const int base = half * HP;
-                store(lo, base, HP);
-                store(hi, base + CPL, HP);
+            if constexpr (D >= 128) dq_swap_stage<true>(x);
+            dq_swap_stage<false>(x);
+            // 4. scale by n / d and store the two runs of 16 coordinates
+            if (token < T) {
+                __half* o = out + ((size_t)tile_local * T + token) * D;
+                auto put = [&](const float* v, int first) {
+                    u4* op = reinterpret_cast<u4*>(o + first);
+#pragma unroll
+                    for (int c = 0; c < 16; c += 8) {
+                        uint32_t qq[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            qq[e] = (uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e] * f)) |
+                                    ((uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e + 1] * f)) << 16);
+                        op[c / 8] = u4{qq[0], qq[1], qq[2], qq[3]};
+                    }
+                };
+                put(x, run0);
+                put(x + 16, D / 2 + run0);
             }
-        } else {
-            if (cur.valid) store(x, coord0, CPL);
         }
         if (next >= n_items) break;
         item = next;
@@ -252,8 +257,7 @@ hipError_t launch_dequant_k(const uint8_t* pool, void* k_fp16, const PoolGeom& g
 hipError_t launch_dequant_v(const uint8_t* pool, void* v_fp16, const PoolGeom& g,
                             const CodebookHalf& cb, int32_t layer_begin, int32_t layer_count,
                             hipStream_t s) {
-    const uint32_t gpw = g.head_dim == 64 ? 2u : 1u;
-    const uint32_t items_per_tile = ((uint32_t)g.n_groups + gpw - 1) / gpw;
+    const uint32_t items_per_tile = (uint32_t)g.n_groups;
     const uint64_t items = (uint64_t)layer_count * g.n_kv_heads * items_per_tile;
     // waves walk the items with a grid stride; 2048 workgroups (8 per CU) cover the chip
     const uint32_t blocks = (uint32_t)std::min<uint64_t>((items + 3) / 4, 2048);
