@@ -4,7 +4,8 @@
 // scored against every pool token: S = scale * q . (code * s), an online softmax runs over
 // token chunks, and P.V is accumulated in the Hadamard-rotated domain as
 // acc = sum_t p_t * n_t * c[code_t]; each output row is H acc / (d * l) with a single
-// inverse FWHT per row instead of one per token.
+// inverse FWHT per row instead of one per token. A launch serves up to 64 of a tile's rows
+// (a range given by the launch arguments); more rows are served by further launches.
 //
 // One workgroup (256 threads) owns one tile. Per chunk of C tokens the keys are expanded
 // to fp32 (already multiplied by their block scale and scale * log2 e) and the values to

@@ -5,7 +5,8 @@
 // M side of two contractions against the tile's tokens: scores S = scale * q . k_hat
 // (keys: int8 q8_0 codes times their fp16 block scale) and P.V in the Hadamard-rotated
 // domain, acc = sum_t p_t n_t c[code_t]; one inverse FWHT per output row at the end
-// replaces the per-token inverse rotation.
+// replaces the per-token inverse rotation. A launch serves up to 64 of a tile's rows (a
+// range given by the launch arguments); more rows are served by further launches.
 //
 // Layout of the work (one workgroup per tile, four token streams, one per SIMD):
 // - the tile's tokens are cut into 32-token chunks (one value bit-plane group each);
