@@ -316,7 +316,9 @@ int polykv_attend_shared_lse(const void* pool, const polykv_layout_t* layout,
 /*
  * As polykv_attend_shared_lse over tokens [0, n_valid) of every tile only, for a pool that
  * is filled by polykv_append_k/v up to n_valid tokens (1 <= n_valid <= n_tokens). Tokens
- * at or past n_valid are never used, whatever their bytes hold.
+ * at or past n_valid are never used, whatever their bytes hold, and no byte of a token at
+ * or past n_valid rounded up to a multiple of 32 is read: the call may run concurrently
+ * with an append whose chunk starts there or later.
  * Errors: as polykv_attend_shared_path; RANGE also for n_valid outside [1, n_tokens].
  */
 int polykv_attend_shared_prefix(const void* pool, const polykv_layout_t* layout,
