@@ -12,7 +12,8 @@
 // Work layout: one workgroup per (256-token tile, head, K or V), eight waves. The reduction
 // over the hidden size runs in 64-wide steps: both operand tiles ([256 tokens][64] of x and
 // [d outputs][64] of W, k-contiguous, 16-byte pieces XOR-swizzled by row) stream into a
-// three-deep LDS ring by direct-to-LDS loads issued two steps ahead, one barrier per step.
+// three-deep LDS ring by direct-to-LDS loads issued two steps ahead, spread over the
+// sub-steps of the step in between, with one barrier per step.
 // Wave w multiplies a 64-token x 64-output block (32-token x 64-output for d = 64) with
 // v_mfma_f32_32x32x16_f16 (fp16 operands, fp32 accumulation), two by two 32 x 32 tiles, so
 // every operand fragment read from LDS feeds two products. After the last step the
@@ -78,29 +79,44 @@ struct PjArgs {
 
 enum { MODE_STORE = 0, MODE_POOL = 1 };
 
-// One step's operand tiles into ring stage `st` by direct-to-LDS loads. Destination piece P
-// (16 bytes, lane-linear within each 1 KB instruction) is row P / 8, slot P % 8 of its
-// tile; it holds global piece (P % 8) ^ ((row >> 1) & 7) of that row, which realises the
-// swizzle of sw_off. Rows past the chunk read its last row (valid memory; their results
-// are not stored).
+// A step's operand tiles go into a ring stage by direct-to-LDS loads, LOADS instructions per
+// wave: instruction j < X_INSTR is x-tile instruction w + WAVES j, the others W-tile
+// instructions. Destination piece P (16 bytes, lane-linear within each 1 KB instruction) is
+// row P / 8, slot P % 8 of its tile; it holds global piece (P % 8) ^ ((row >> 1) & 7) of
+// that row, which realises the swizzle of sw_off. Rows past the chunk read its last row
+// (valid memory; their results are not stored). The per-lane offsets are fixed over the
+// reduction (the scalar base moves by k0), so they are computed once.
 template <class C>
-__device__ __forceinline__ void issue_step(const __half* xt, const __half* wmat, int hidden, int k0,
-                                           int rows_valid, int w, uint8_t* stage) {
-    const uint32_t lane = lds_dma::lane_id();
+struct DmaOffs {
+    uint32_t o[C::LOADS];
+};
+template <class C>
+__device__ __forceinline__ DmaOffs<C> dma_offsets(int hidden, int rows_valid, int w, int lane) {
+    DmaOffs<C> d;
     const uint32_t row_bytes = (uint32_t)hidden * 2u;
 #pragma unroll
-    for (int i = 0; i < C::X_INSTR; ++i) {
-        const int q = w + C::WAVES * i;                    // instruction index within the x tile
-        const uint32_t P = 64u * (uint32_t)q + lane, r = P >> 3, c = (P & 7u) ^ ((r >> 1) & 7u);
-        const uint32_t rr = min(r, (uint32_t)rows_valid - 1u);
-        lds_dma::dma16(xt + k0, rr * row_bytes + 16u * c, lds_dma::lds_addr(stage + 1024 * q));
+    for (int j = 0; j < C::LOADS; ++j) {
+        const bool isx = j < C::X_INSTR;
+        const int q = w + C::WAVES * (isx ? j : j - C::X_INSTR);
+        const uint32_t P = 64u * (uint32_t)q + (uint32_t)lane, r = P >> 3, c = (P & 7u) ^ ((r >> 1) & 7u);
+        const uint32_t rr = isx ? min(r, (uint32_t)rows_valid - 1u) : r;
+        d.o[j] = rr * row_bytes + 16u * c;
     }
-#pragma unroll
-    for (int i = 0; i < C::W_INSTR; ++i) {
-        const int q = w + C::WAVES * i;
-        const uint32_t P = 64u * (uint32_t)q + lane, r = P >> 3, c = (P & 7u) ^ ((r >> 1) & 7u);
-        lds_dma::dma16(wmat + k0, r * row_bytes + 16u * c, lds_dma::lds_addr(stage + C::X_BYTES + 1024 * q));
-    }
+    return d;
+}
+// Instruction j of a step's loads is issued during sub-step sched(j) of the step two before,
+// between that sub-step's fragment reads and its products. Issued in one burst after the
+// barrier, every wave's loads (40 or 48 instructions) queue at the CU's memory unit at once
+// and a wave held at one of them issues no products; spread out, they overlap the products.
+template <class C>
+__device__ __forceinline__ constexpr int sched(int j) { return j * (BK / 16) / C::LOADS; }
+template <class C>
+__device__ __forceinline__ void issue_one(const __half* xt, const __half* wmat, int k0, int j, int w,
+                                          const DmaOffs<C>& d, uint8_t* stage) {
+    const bool isx = j < C::X_INSTR;
+    const int q = w + C::WAVES * (isx ? j : j - C::X_INSTR);
+    if (isx) lds_dma::dma16(xt + k0, d.o[j], lds_dma::lds_addr(stage + 1024 * q));
+    else lds_dma::dma16(wmat + k0, d.o[j], lds_dma::lds_addr(stage + C::X_BYTES + 1024 * q));
 }
 
 // One 32-token group of the projected block (fp16 in LDS, [32 tokens][D]): written as fp16
@@ -187,20 +203,24 @@ __global__ __launch_bounds__(PjCfg<D>::THREADS, 1) void k_project(PjArgs a) {
         for (int j = 0; j < NT; ++j) acc[i][j] = f16v{};
 
     // ring of NST stages: step ks multiplies stage ks % NST; the loads of step ks + NST - 1
-    // go into the stage step ks - 1 used, after the barrier that ends every wave's reads of it
+    // go into the stage step ks - 1 used, after the barrier that ends every wave's reads of
+    // it, spread over the sub-steps of step ks
+    const DmaOffs<C> dof = dma_offsets<C>(hidden, rows_valid, w, lane);
     const int steps = hidden / BK;
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
-        if (s < steps) issue_step<C>(xt, wmat, hidden, s * BK, rows_valid, w, lds + s * C::STAGE_BYTES);
+        if (s < steps)
+#pragma unroll
+            for (int j = 0; j < C::LOADS; ++j) issue_one<C>(xt, wmat, s * BK, j, w, dof, lds + s * C::STAGE_BYTES);
     for (int ks = 0; ks < steps; ++ks) {
         // this step's loads (and those of every earlier step) have landed, in every wave:
         // only the next step's may still be in flight
         if (ks + 1 < steps) lds_dma::wait_vm<C::LOADS>();
         else lds_dma::wait_vm<0>();
         __syncthreads();
-        if (ks + NST - 1 < steps)
-            issue_step<C>(xt, wmat, hidden, (ks + NST - 1) * BK, rows_valid, w,
-                          lds + ((ks + NST - 1) % NST) * C::STAGE_BYTES);
+        const bool more = ks + NST - 1 < steps;
+        uint8_t* nst = lds + ((ks + NST - 1) % NST) * C::STAGE_BYTES;
+        const int nk0 = (ks + NST - 1) * BK;
         const uint8_t* xs = lds + (ks % NST) * C::STAGE_BYTES;
         const uint8_t* ws = xs + C::X_BYTES;
 #pragma unroll
@@ -214,6 +234,10 @@ __global__ __launch_bounds__(PjCfg<D>::THREADS, 1) void k_project(PjArgs a) {
 #pragma unroll
             for (int j = 0; j < NT; ++j)
                 bv[j] = *reinterpret_cast<const h8*>(ws + sw_off(col0 + 32u * j + (lane & 31), c));
+            if (more)
+#pragma unroll
+                for (int j = 0; j < C::LOADS; ++j)
+                    if (sched<C>(j) == ss) issue_one<C>(xt, wmat, nk0, j, w, dof, nst);
 #pragma unroll
             for (int i = 0; i < MT; ++i)
 #pragma unroll
