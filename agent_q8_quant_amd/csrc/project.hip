@@ -104,12 +104,14 @@ __device__ __forceinline__ DmaOffs<C> dma_offsets(int hidden, int rows_valid, in
     }
     return d;
 }
-// Instruction j of a step's loads is issued during sub-step sched(j) of the step two before,
-// between that sub-step's fragment reads and its products. Issued in one burst after the
-// barrier, every wave's loads (40 or 48 instructions) queue at the CU's memory unit at once
-// and a wave held at one of them issues no products; spread out, they overlap the products.
+// Instruction j of a step's loads is issued during sub-step sched(j) (1, 2 or 3) of the step
+// two before, between that sub-step's fragment reads and its products. Issued in one burst
+// after the barrier, every wave's loads (40 or 48 instructions) queue at the CU's memory
+// unit at once and a wave held at one of them issues no products; spread out, they overlap
+// the products. Sub-step 0 is left out: every wave reads its first fragments right after
+// the barrier.
 template <class C>
-__device__ __forceinline__ constexpr int sched(int j) { return j * (BK / 16) / C::LOADS; }
+__device__ __forceinline__ constexpr int sched(int j) { return 1 + j * (BK / 16 - 1) / C::LOADS; }
 template <class C>
 __device__ __forceinline__ void issue_one(const __half* xt, const __half* wmat, int k0, int j, int w,
                                           const DmaOffs<C>& d, uint8_t* stage) {

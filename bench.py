@@ -620,11 +620,13 @@ def main():
         pj_ev = {"fused": [], "unfused": [], "library": []}
         if proj is not None:
             px, pwk, pwv, _, _ = proj
-            w_t = torch.cat([pwk, pwv]).t().contiguous()   # [hidden][2 H d], a plain 2-D GEMM
+            # [2 H d][hidden] row-major, as the kernel reads it: x W^T with W^T a transposed
+            # view (the library's faster layout for this shape), one 2-D GEMM per layer
+            w_kv = torch.cat([pwk, pwv])
 
             def project_library(i):
                 for l in range(cfg.n_layers):
-                    torch.matmul(px, w_t)
+                    torch.matmul(px, w_kv.t())
             for name, fn in (("fused", project_fused), ("unfused", project_unfused), ("library", project_library)):
                 fn(0)
                 for i in range(2):
