@@ -627,9 +627,13 @@ def main():
             def project_library(i):
                 for l in range(cfg.n_layers):
                     torch.matmul(px, w_kv.t())
-            for name, fn in (("fused", project_fused), ("unfused", project_unfused), ("library", project_library)):
+            # the three in turn, three rounds, so that the chip's state (clock, temperature)
+            # weighs on each alike
+            runs = (("fused", project_fused), ("unfused", project_unfused), ("library", project_library))
+            for _, fn in runs:
                 fn(0)
-                for i in range(2):
+            for i in range(3):
+                for name, fn in runs:
                     e0 = ev()
                     fn(i)
                     e1 = ev()
@@ -760,13 +764,16 @@ def main():
                             "kernels": ["compress_k", "compress_v"], "us": t_app["separate"] * 1e6,
                             "frac_hbm": compress_bytes / t_app["separate"] / 1e9 / HBM_PEAK_GBPS}}
     if pj_ev["fused"]:
-        t_f = sum(a.elapsed_time(b) for a, b in pj_ev["fused"]) / len(pj_ev["fused"]) / 1e3
-        t_u = sum(a.elapsed_time(b) for a, b in pj_ev["unfused"]) / len(pj_ev["unfused"]) / 1e3
+        def med_s(evs):  # median over the rounds, seconds
+            t = sorted(a.elapsed_time(b) for a, b in evs)
+            return t[len(t) // 2] / 1e3
+        t_f = med_s(pj_ev["fused"])
+        t_u = med_s(pj_ev["unfused"])
         flops = 2.0 * cfg.n_layers * cfg.n_tokens * hidden * 2 * cfg.n_kv_heads * cfg.head_dim
         result["project_compress"] = {
             "kernel": "project (fused)", "hidden": hidden, "layers": cfg.n_layers,
             "us_fused": t_f * 1e6, "us_unfused": t_u * 1e6,
-            "us_library_gemm_only": sum(a.elapsed_time(b) for a, b in pj_ev["library"]) / len(pj_ev["library"]) * 1e3,
+            "us_library_gemm_only": med_s(pj_ev["library"]) * 1e6,
             "roofline": {"bound": "mfma", "achieved": flops / t_f / 1e12, "peak": 2500.0,
                          "unit": "TFLOP/s", "frac": flops / t_f / 1e12 / 2500.0},
             "flops": flops}
