@@ -71,7 +71,11 @@ __global__ __launch_bounds__(256) void k_dequant_k(const uint8_t* __restrict__ p
 //    bit both values of its local coordinate e and the other lane both values of e + 16, so
 //    each swap stage halves the run a lane holds; a lane ends with two runs of 16 coordinates,
 //    c0 .. c0 + 15 and d/2 + c0 .. + 15;
-// 4. times n / d, rounded to fp16, stored as 16-byte pieces.
+// 4. times n / d, rounded to fp16; for d >= 128 through the wave's LDS rows out to memory:
+//    each lane places its two runs in its token's row, then lane l writes pieces l, l + 64,
+//    ... of the pass's rows, so every store instruction covers 1 KB of consecutive bytes (a
+//    lane's own runs are 16-byte pieces 32 bytes apart, which a store instruction would
+//    scatter over 16 rows at d = 128); at d = 64 the lanes store their own runs.
 // Keeping 32 coordinates per lane (not d/2) halves the registers of d = 128 and so doubles
 // the waves a SIMD holds, which hides the latency of the lookup and shuffle chains.
 // ---------------------------------------------------------------------------------------
@@ -83,6 +87,12 @@ struct DqCfg {
     static constexpr int WORDS = 3 * D;              // plane words per group
     static constexpr int PIECES = WORDS / 4;         // 16-byte pieces per group
     static constexpr int PPL = (PIECES + 63) / 64;   // pieces per lane
+    // output staging of one pass (TPP tokens x D fp16): rows padded by 16 bytes so that the
+    // 16 lanes of one 16-byte LDS access (same q, consecutive t) hit distinct banks
+    static constexpr int ROW_BYTES = 2 * D + 16;
+    static constexpr int OUT_BYTES = TPP * ROW_BYTES;
+    static constexpr int OUT_PIECES = TPP * D / 8;    // 16-byte pieces of a pass (= 4 per lane)
+    static_assert(OUT_PIECES == 256, "four pieces per lane");
 };
 
 // first coordinate of the lane's lower run after the cross-lane stages (q: the lane's
@@ -116,6 +126,7 @@ __global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ p
     using C = DqCfg<D>;
     constexpr int TPP = C::TPP, PASSES = C::PASSES;
     __shared__ __attribute__((aligned(16))) uint32_t words[4][C::WORDS];
+    __shared__ __attribute__((aligned(16))) uint8_t ostage[4][D >= 128 ? C::OUT_BYTES : 16];
     __shared__ float ctab[8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -180,7 +191,6 @@ __global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ p
 #pragma unroll
         for (int pass = 0; pass < PASSES; ++pass) {
             const int t = TPP * pass + tl;  // token within the group
-            const int token = 32 * g0 + t;
             const float f = __half2float(__ushort_as_half((unsigned short)ncur[pass])) * (1.0f / (float)D);
             // 2. codes -> centroids
             float x[32];
@@ -218,23 +228,46 @@ __global__ __launch_bounds__(256) void k_dequant_v(const uint8_t* __restrict__ p
             }
             if constexpr (D >= 128) dq_swap_stage<true>(x);
             dq_swap_stage<false>(x);
-            // 4. scale by n / d and store the two runs of 16 coordinates
-            if (token < T) {
-                __half* o = out + ((size_t)tile_local * T + token) * D;
-                auto put = [&](const float* v, int first) {
-                    u4* op = reinterpret_cast<u4*>(o + first);
+            // 4. times n / d, rounded once to fp16. For d >= 128 the lane's two runs of 16
+            //    coordinates go to their places in the pass's rows in LDS (row tl), and the
+            //    wave then writes the rows out as consecutive 16-byte pieces (one store
+            //    instruction covers 1 KB); for d = 64 (128-byte rows) each lane stores its
+            //    runs itself.
+            const int tok0 = 32 * g0 + TPP * pass;                // first token of the pass
+            auto put = [&](const float* v, int first, uint8_t* row_base) {
 #pragma unroll
-                    for (int c = 0; c < 16; c += 8) {
-                        uint32_t qq[4];
+                for (int c = 0; c < 16; c += 8) {
+                    uint32_t qq[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            qq[e] = (uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e] * f)) |
-                                    ((uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e + 1] * f)) << 16);
-                        op[c / 8] = u4{qq[0], qq[1], qq[2], qq[3]};
-                    }
-                };
-                put(x, run0);
-                put(x + 16, D / 2 + run0);
+                    for (int e = 0; e < 4; ++e)
+                        qq[e] = (uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e] * f)) |
+                                ((uint32_t)__half_as_ushort(__float2half_rn(v[c + 2 * e + 1] * f)) << 16);
+                    *reinterpret_cast<u4*>(row_base + 2 * (first + c)) = u4{qq[0], qq[1], qq[2], qq[3]};
+                }
+            };
+            if constexpr (D >= 128) {
+                uint8_t* rowp = &ostage[w][0] + tl * C::ROW_BYTES;
+                put(x, run0, rowp);
+                put(x + 16, D / 2 + run0, rowp);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                u4* ob = reinterpret_cast<u4*>(out + ((size_t)tile_local * T + tok0) * D);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int piece = 64 * k + lane, row = piece / (D / 8), pc = piece % (D / 8);
+                    const u4 val = *reinterpret_cast<const u4*>(&ostage[w][0] + row * C::ROW_BYTES + 16 * pc);
+                    if (tok0 + row < T) ob[piece] = val;
+                }
+                // the next pass rewrites the rows: these reads are complete once their values
+                // are stored (each store waits for its value)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            } else if (tok0 + tl < T) {
+                uint8_t* rowp = reinterpret_cast<uint8_t*>(out + ((size_t)tile_local * T + tok0 + tl) * D);
+                put(x, run0, rowp);
+                put(x + 16, D / 2 + run0, rowp);
             }
         }
         if (next >= n_items) break;
