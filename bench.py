@@ -536,6 +536,24 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
 
+        # Secondary figure: one step's D decode launches captured in a HIP graph and replayed
+        # (the same kernels and pools as the eager launches above, without host work per
+        # launch; every kernel has run eagerly before the capture)
+        graph_ev = []
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for s in range(D):
+                decode((1 + s) % n_pools, s)
+        gr.replay()
+        for _ in range(3):
+            e0 = ev()
+            gr.replay()
+            e1 = ev()
+            graph_ev.append((e0, e1))
+        stream.synchronize()
+        graph_us = sorted(a.elapsed_time(b) * 1e3 / D for a, b in graph_ev)[1]
+        del gr
+
         # Secondary figures: single decode launches right after evicting the 256 MB Infinity
         # Cache with 1 GiB of other traffic, outside the events: a 1 GiB read (the pool then
         # comes from HBM), and a 1 GiB write (which also leaves that cache full of dirty
@@ -731,6 +749,8 @@ def main():
             "GBps_both": compress_bytes / (t_ck + t_cv) / 1e9},
         "wall_ms_per_step": wall / args.steps * 1e3,
     }
+    result["decode_graph"] = {"what": "one step's decode launches captured in a HIP graph, replayed (median of 3)",
+                              "us_per_launch": graph_us}
     if cold_us["read"]:
         result["decode_us_after_1GiB_read"] = cold_us["read"]
         result["decode_us_after_1GiB_write"] = cold_us["write"]
