@@ -23,7 +23,10 @@
  *    codebook structs are HOST pointers. The caller allocates and owns every buffer; the
  *    library never allocates, frees or synchronises, and keeps no per-call state.
  *  - hip_stream is a hipStream_t (NULL = the null stream). All device work is
- *    asynchronous on it; buffers must stay alive until that work has completed.
+ *    asynchronous on it; buffers must stay alive until that work has completed. The
+ *    device work of a call is kernel launches only (no copies or memsets), so a call
+ *    may be captured into a HIP graph once every kernel it launches has been launched
+ *    eagerly on the device (the first launch of a kernel sets its LDS limit).
  *  - All arguments are validated on the host before anything is launched, so an error
  *    return means nothing was enqueued. Non-finite inputs are not checked: the results
  *    for them are unspecified.
